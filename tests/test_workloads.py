@@ -1,0 +1,71 @@
+"""The seeded input generator (CPU only): determinism, sizes, placement and poison."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(10000).astype(np.float32),
+                        np.array([1.0 + 2**-8, 1.0 + 3 * 2**-8, -(1.0 + 2**-8), 3.0e38, 1e-40], np.float32)])
+    ours = wl.f32_to_bf16_bits(x)
+    theirs = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, theirs)
+
+
+@pytest.mark.parametrize("name", ["gpt2_fp32_ctx32", "gpt2_bf16_b8", "qwen3_8b_b1_ctx4096"])
+def test_case_layout_and_poison(name):
+    w = wl.WORKLOADS[name]
+    c = wl.make_case(w)
+    c2 = wl.make_case(w)
+    for a, b in [(c.q, c2.q), (c.k_cache, c2.k_cache), (c.v_new, c2.v_new), (c.block_tables, c2.block_tables)]:
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    B, Hq, Hkv, D, BS = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    assert c.q.shape == (B, Hq, D) and c.k_new.shape == (B, Hkv, D)
+    assert c.k_cache.shape == (c.num_blocks, Hkv, BS, D)
+    assert c.block_tables.shape == (B, w.max_blocks_per_seq)
+    isnan = lambda a: np.isnan(a) if a.dtype == np.float32 else ((a & 0x7F80) == 0x7F80) & ((a & 0x7F) != 0)  # noqa
+    owned = np.zeros(c.k_cache.shape, bool)
+    used = set()
+    for b in range(B):
+        L = int(c.context_lens[b])
+        n = -(-L // BS)
+        ids = c.block_tables[b, :n]
+        assert np.all(c.block_tables[b, n:] == -1)
+        used.update(ids.tolist())
+        for t in range(L - 1):
+            owned[ids[t // BS], :, t % BS, :] = True
+    assert len(used) == sum(-(-int(L) // BS) for L in c.context_lens)  # no block shared
+    assert not np.any(isnan(c.k_cache) & owned) and not np.any(isnan(c.v_cache) & owned)
+    assert np.all(isnan(c.k_cache)[~owned]) and np.all(isnan(c.v_cache)[~owned])
+
+
+def test_sizes_of_big_workloads():
+    # Layouts only (no values), checked against the sizes the workloads are quoted with.
+    w4 = wl.WORKLOADS["qwen3_8b_b64"]
+    lay = wl.make_layout(w4, np.random.default_rng(w4.seed))
+    L = lay.context_lens
+    assert L.shape == (64,) and L.min() >= 128 and L.max() <= 8192
+    need = int(lay.blocks_per_seq.sum())
+    assert lay.num_blocks == math.ceil(1.25 * need)
+    w5 = wl.WORKLOADS["qwen3_8b_b4_long"]
+    lay5 = wl.make_layout(w5, np.random.default_rng(w5.seed))
+    assert lay5.num_blocks == 6400 and list(lay5.context_lens) == [8192, 16384, 24576, 32768]
+    w3 = wl.WORKLOADS["qwen3_8b_b1_ctx4096"]
+    assert wl.make_layout(w3, np.random.default_rng(w3.seed)).num_blocks == 320
+
+
+def test_rmsnorm_rows():
+    c = wl.make_case(wl.WORKLOADS["qwen3_8b_b1_ctx4096"].with_(ctx=("fixed", [40]), max_blocks_per_seq=4))
+    q = torch.from_numpy(c.q.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    # Each row is x * gain with unit-RMS x and gain ~ N(1, 0.1): row RMS stays near 1.
+    rms = np.sqrt((q ** 2).mean(-1))
+    assert np.all(np.abs(rms - 1) < 0.2)
+    # All rows share one gain vector, so the per-column RMS over rows deviates coherently.
+    col = np.sqrt((q.reshape(-1, q.shape[-1]) ** 2).mean(0))
+    assert col.std() > 0.03
