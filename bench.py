@@ -1,0 +1,260 @@
+"""Decode-step benchmark on one MI355X: KV append + split-K paged decode attention + LSE reduce.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--partition P] [--copies R]
+
+Prints ONE JSON line on stdout (diagnostics go to stderr):
+  value         K+V bytes the step must stream / measured step time, in GB/s (whole job, 1 GPU)
+  ms_per_step   mean wall time of one step on the GPU (HIP events around K back-to-back steps)
+  seqs_per_s    batch / step time
+  roofline      the decode kernel alone: its algorithmic bytes per launch / its mean duration
+                (HIP events around each decode launch, on the launch stream) vs 8 TB/s;
+                `traffic` comes from the rocprofv3 FETCH_SIZE/WRITE_SIZE summary committed
+                in profiles/, and is null when the kernel source changed since it was taken
+  cpu_baseline  the fp64 oracle timed on the host over a bounded sample of the same workload;
+                its output is also compared with the GPU's for those sequences
+
+Inputs are generated once and resident in HBM before timing. The pools exist in R copies
+(default: enough that R x pool > 3 GB), and step k reads copy k % R. Each step therefore
+streams K/V that no recent step touched, and the 256 MB Infinity Cache cannot serve it.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode attention KV GB/s (% of HBM peak) + seqs/s, Qwen3-8B GQA shape"
+DECODE_SOURCES = ["paged_kv_decode_xs_amd/csrc/xs_decode.hip", "paged_kv_decode_xs_amd/csrc/xs_device.h"]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def decode_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, partition: int):
+    """Per-launch HBM bytes of the decode kernel from the committed rocprofv3 counter summary."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("decode_source_sha256") != decode_source_hash() or kv.get("partition_size") != str(partition):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def algorithmic_bytes(case, partition: int):
+    """Bytes the step must move, by kernel (the method's own data, nothing padded)."""
+    w = case.workload
+    L = case.context_lens.astype(np.int64)
+    B, Hq, Hkv, D, BS, e = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.elt_bytes
+    kv = int(L.sum()) * Hkv * D * e * 2
+    ids = 4 * int(((L + BS - 1) // BS).sum())
+    q = B * Hq * D * e
+    out = B * Hq * D * e
+    lens = 4 * B
+    if partition > 0:
+        nparts = int(((L + partition - 1) // partition).sum())
+        partials = nparts * Hq * (D + 2) * 4
+        decode = kv + ids + q + lens + partials
+        reduce = partials + lens + out
+    else:
+        decode = kv + ids + q + lens + out
+        reduce = 0
+    append = 4 * B * Hkv * D * e + 4 * B + lens  # read k_new/v_new, write their slots, one block id per sequence
+    return {"kv": kv, "decode": decode, "reduce": reduce, "append": append, "step": decode + reduce + append}
+
+
+def cpu_baseline(case, gpu_out, budget_s: float):
+    """Time the fp64 oracle over whole sequences until the time budget is used; compare outputs."""
+    import oracle  # the oracle is test infrastructure; this leg is the only bench code that uses it
+
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((i.get("num_threads") or 1) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:  # noqa: BLE001
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    w = case.workload
+    k_pool, v_pool = oracle.kv_append(case.k_cache, case.v_cache, case.k_new, case.v_new, case.block_tables,
+                                      case.context_lens, w.block_size)
+    done, kv_bytes, elapsed, max_err, bad = 0, 0, 0.0, 0.0, 0
+    for b in range(w.batch):
+        sl = slice(b, b + 1)
+        t0 = time.perf_counter()
+        ref = oracle.paged_decode_attention(case.q[sl], k_pool, v_pool, case.block_tables[sl],
+                                            case.context_lens[sl], w.scale, w.block_size, w.dtype)
+        elapsed += time.perf_counter() - t0
+        kv_bytes += int(case.context_lens[b]) * w.num_kv_heads * w.head_dim * w.elt_bytes * 2
+        got = gpu_out[b:b + 1]
+        err = np.abs(got - ref)
+        atol, rtol = (1e-5, 0.0) if w.dtype == "f32" else (2e-2, 2e-2)
+        bad += int(np.sum(~(err <= atol + rtol * np.abs(ref))))
+        max_err = max(max_err, float(err.max()) if err.size else 0.0)
+        done += 1
+        if elapsed >= budget_s:
+            break
+    return {
+        "value": round(kv_bytes / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle attention over the first {done} of {w.batch} sequences "
+                  f"({int(case.context_lens[:done].sum())} tokens, {kv_bytes / 1e6:.1f} MB of K+V), "
+                  f"{elapsed:.2f} s; K+V bytes of the sample / oracle time",
+        "seconds": round(elapsed, 3),
+    }, {"sequences_checked": done, "max_abs_err": max_err, "out_of_tolerance": bad}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen3_8b_b64")
+    ap.add_argument("--partition", type=int, default=None, help="split-K partition size (0 = no split)")
+    ap.add_argument("--copies", type=int, default=None, help="pool copies to rotate through")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: every step runs on a single device "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import paged_kv_decode_xs_amd as xs
+    import workloads as wl
+    from workloads.device import case_to_device
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    xs.load_library()  # raises if libxs.so is missing: there is no fallback path
+
+    w = wl.WORKLOADS[args.workload]
+    P = w.partition_size if args.partition is None else args.partition
+    t0 = time.time()
+    case = wl.make_case(w)
+    log(f"[bench] {w.name}: generated in {time.time() - t0:.1f}s, NB={case.num_blocks}, "
+        f"sum L={int(case.context_lens.sum())}, K+V={case.kv_bytes() / 1e9:.3f} GB")
+    dev = case_to_device(case, "cuda:0")
+    pool_bytes = 2 * dev["k_cache"].numel() * dev["k_cache"].element_size()
+    R = args.copies or max(2, math.ceil(3e9 / pool_bytes))
+    pools = [(dev["k_cache"], dev["v_cache"])] + [(dev["k_cache"].clone(), dev["v_cache"].clone())
+                                                   for _ in range(R - 1)]
+    maxlen = int(case.context_lens.max())
+    steps = [xs.DecodeStep(dev["q"], kc, vc, dev["block_tables"], dev["context_lens"], dev["k_new"], dev["v_new"],
+                           w.scale, partition_size=P, max_context_len=maxlen) for kc, vc in pools]
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        steps[i % R].run(stream)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        s = steps[i % R]
+        s.append(stream)
+        ev[i][0].record(stream)
+        s.attend(stream)
+        ev[i][1].record(stream)
+        s.reduce(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / K
+    decode_ms = [a.elapsed_time(b) for a, b in ev]
+    decode_ms_mean = float(np.mean(decode_ms))
+
+    ab = algorithmic_bytes(case, P)
+    kv_gbs = ab["kv"] / (ms_step * 1e-3) / 1e9
+    achieved = ab["decode"] / (decode_ms_mean * 1e-3) / 1e9
+    traffic = read_traffic(w.name, P)
+    result = {
+        "metric": METRIC,
+        "value": round(kv_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "batch": w.batch,
+            "num_q_heads": w.num_q_heads,
+            "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim,
+            "block_size": w.block_size,
+            "context_lens": f"{w.ctx[0]} {list(w.ctx[1:])}, seed {w.seed}",
+            "partition_size": P,
+            "pool_copies_rotated": R,
+            "kv_bytes_per_step": ab["kv"],
+            "step": "kv_append + paged_attn_decode + paged_attn_reduce",
+        },
+        "seqs_per_s": round(w.batch / (ms_step * 1e-3), 1),
+        "pct_of_hbm_peak": round(100 * kv_gbs / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "paged_decode_kernel",
+            "algorithmic_bytes_per_launch": ab["decode"],
+            "mean_launch_us": round(decode_ms_mean * 1e3, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        out = steps[(K - 1) % R].out.float().cpu().double().numpy()
+        cpu, parity = cpu_baseline(case, out, args.cpu_budget)
+        result["cpu_baseline"] = cpu
+        result["parity_vs_oracle"] = parity
+        if parity["out_of_tolerance"]:
+            log(f"[bench] PARITY FAILURE: {parity}")
+    print(json.dumps(result), flush=True)
+    return 0 if result.get("parity_vs_oracle", {}).get("out_of_tolerance", 0) == 0 else 3
+
+
+if __name__ == "__main__":
+    sys.exit(main())

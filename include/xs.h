@@ -1,0 +1,138 @@
+/*
+ * xs.h - C ABI of libxs.so: paged-KV decode attention for AMD MI355X (gfx950).
+ *
+ * One decode step of an LLM serving engine over a paged KV cache:
+ *   1. xs_kv_append          writes each running sequence's new K/V row into its block.
+ *   2. xs_paged_attn_decode  computes GQA softmax(q K^T * scale) V for every (sequence,
+ *                            query head), optionally per split-K partition of the context.
+ *   3. xs_paged_attn_reduce  merges the partitions with a log-sum-exp rule.
+ *
+ * Sources: the xserv pages (gitea compare views of the xserv engine).
+ *   - Pool layout, block table, context_lens, q/out shapes, the append and decode
+ *     contracts: xserv compare phase10...cf1e9e41, crates/xserv-kernels/src/attention.rs,
+ *     FFI block and doc comments of `reshape_and_cache_bf16`,
+ *     `reshape_and_cache_batched_bf16` and `paged_decode_attention`.
+ *   - GQA mapping (query head h reads kv head h / n_rep, n_rep = Hq / Hkv): xserv compare
+ *     phase8...phase13, `repeat_kv` in the Qwen3 model and the `repeat_kv_bf16` kernel.
+ *   - Split-K partitions and the log-sum-exp merge are not on the pages. They are this
+ *     library's way to spread long contexts over the GPU. The merge is an exact identity of
+ *     the unsplit softmax.
+ *
+ * Common conventions
+ *   - Every pointer is a device pointer on the current HIP device, except where stated.
+ *     The caller owns every buffer. The library allocates nothing, never synchronizes,
+ *     and enqueues all work on `stream` (a hipStream_t passed as void*; NULL = null stream).
+ *   - Shapes are row-major (C-contiguous):
+ *       q, out          [batch, num_q_heads, head_dim]          (one query token per sequence)
+ *       k_new, v_new    [batch, num_kv_heads, head_dim]
+ *       k_cache/v_cache [num_blocks, num_kv_heads, block_size, head_dim]
+ *       block_tables    int32 [batch, max_blocks_per_seq]; entry j of row b is the physical
+ *                       block holding tokens [j*block_size, (j+1)*block_size) of sequence b.
+ *       context_lens    int32 [batch]; L_b = the context length of sequence b AFTER this
+ *                       step's append, i.e. the index of the just-written token + 1.
+ *   - dtype: q, k_new, v_new, the pools and out all have the same dtype (XS_F32 or XS_BF16).
+ *     Arithmetic is fp32. bf16 results are rounded to nearest-even.
+ *   - Supported: head_dim in {64, 128}; block_size in {8, 16, 32}; num_q_heads a multiple
+ *     of num_kv_heads; q, pools, k_new/v_new, out and part_o 16-byte aligned.
+ *   - Return value: XS_OK (0) or an xs_status. A nonzero status sets a message that
+ *     xs_last_error() returns. Host-checkable argument errors are reported before any HIP
+ *     call is made. A failed launch gives XS_ELAUNCH.
+ *   - Device-resident preconditions cannot be checked on the host: 0 <= L_b <= max_blocks_per_seq
+ *     * block_size, and the block ids in use lie in [0, num_blocks). Violating them gives
+ *     undefined results but no out-of-bounds access. The kernels clamp L_b to
+ *     max_blocks_per_seq * block_size, skip blocks whose id lies outside [0, num_blocks),
+ *     and treat L_b <= 0 as an empty context.
+ */
+#ifndef XS_H
+#define XS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { XS_F32 = 0, XS_BF16 = 1 } xs_dtype;
+
+typedef enum {
+  XS_OK = 0,
+  XS_EINVAL = 1,       /* a null pointer, a bad size, a misaligned pointer */
+  XS_EUNSUPPORTED = 2, /* a valid request this library does not implement (head_dim, block_size, dtype) */
+  XS_ELAUNCH = 3       /* the HIP runtime rejected a kernel launch */
+} xs_status;
+
+/*
+ * Decode-step KV append (xserv compare phase10...cf1e9e41, attention.rs,
+ * `reshape_and_cache_batched_bf16` and its doc comment).
+ *
+ * For every sequence b with L = context_lens[b] >= 1, position p = L - 1 lies in physical
+ * block blk = block_tables[b, p / block_size] at slot off = p % block_size. For every kv
+ * head g, row k_cache[blk, g, off, :] becomes k_new[b, g, :], and v_cache likewise. This is
+ * a bit-exact copy, and no other byte of the pools changes.
+ * Arguments: k_new, v_new [batch, num_kv_heads, head_dim] (read); k_cache, v_cache (written
+ * in place); block_tables, context_lens (read).
+ * Two sequences must not map the same slot; otherwise the last write wins in no fixed order.
+ * batch == 0 is a no-op.
+ */
+int xs_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                 const int32_t* block_tables, const int32_t* context_lens,
+                 int batch, int num_kv_heads, int head_dim, int block_size,
+                 int max_blocks_per_seq, int num_blocks, int dtype, void* stream);
+
+/*
+ * Single-token GQA decode attention over the paged pool (xserv compare phase10...cf1e9e41,
+ * attention.rs, `paged_decode_attention` and its FFI `launch_paged_decode_attention_bf16`).
+ *
+ * For sequence b, query head h, g = h / (num_q_heads / num_kv_heads), tokens t in [0, L_b):
+ *   K_t = k_cache[block_tables[b, t / block_size], g, t % block_size, :], V_t likewise,
+ *   s_t = scale * dot(q[b, h, :], K_t),
+ *   out[b, h, :] = sum_t exp(s_t - max s) V_t / sum_t exp(s_t - max s).
+ * The single query sits at the last position, so the causal mask lets it see all L_b keys.
+ * Pool slots at t >= L_b are never used, and may hold anything, NaN included.
+ * L_b = 0 gives out[b, h, :] = 0.
+ *
+ * partition_size == 0: no split. `out` is written. part_o/part_m/part_l must be NULL and
+ *   max_partitions is ignored.
+ * partition_size  > 0: split-K. It must be a multiple of block_size. Partition j of sequence b
+ *   covers tokens [j*P, min((j+1)*P, L_b)) for j < n_b = ceil(L_b / P). For each (b, h, j)
+ *   the call writes, in fp32:
+ *     part_m[b, h, j]     = m_j = max_t s_t                          [batch, num_q_heads, NP]
+ *     part_l[b, h, j]     = l_j = sum_t exp(s_t - m_j)               [batch, num_q_heads, NP]
+ *     part_o[b, h, j, :]  = sum_t exp(s_t - m_j) V_t / l_j           [batch, num_q_heads, NP, head_dim]
+ *   with NP = max_partitions. `out` is not touched (it may be NULL); xs_paged_attn_reduce
+ *   produces it. Entries j >= n_b are not written. Partitions at j >= max_partitions are
+ *   not computed, so the caller must give max_partitions >= max_b ceil(L_b / P).
+ */
+int xs_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         float scale, void* out,
+                         float* part_o, float* part_m, float* part_l,
+                         int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                         int block_size, int max_blocks_per_seq, int num_blocks,
+                         int partition_size, int max_partitions, int dtype, void* stream);
+
+/*
+ * Log-sum-exp merge of split-K partitions (not on the pages: the exact identity of the
+ * unsplit softmax). For each (b, h), with n = min(ceil(L_b / P), max_partitions),
+ *   M = max_j m_j,  w_j = l_j exp(m_j - M),  out[b, h, :] = sum_j w_j o_j / sum_j w_j.
+ * Reads part_o/part_m/part_l as written by xs_paged_attn_decode with the same partition_size
+ * and max_partitions. Writes out [batch, num_q_heads, head_dim] in `dtype`. L_b <= 0, or a
+ * sequence whose partitions all have l_j = 0, gives zeros.
+ */
+int xs_paged_attn_reduce(const float* part_o, const float* part_m, const float* part_l,
+                         const int32_t* context_lens, void* out,
+                         int batch, int num_q_heads, int head_dim,
+                         int partition_size, int max_partitions, int dtype, void* stream);
+
+/* Message for the last nonzero status returned on this thread ("" if none). Host memory owned
+ * by the library, valid until the next call on this thread. */
+const char* xs_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int xs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XS_H */

@@ -1,0 +1,20 @@
+"""Paged-KV decode attention for AMD MI355X (gfx950).
+
+The computation lives in libxs.so (hand-written HIP kernels behind the C ABI in include/xs.h).
+This package is its thin Python binding plus a decode-step helper that chains the three calls.
+"""
+
+from ._binding import (  # noqa: F401
+    XS_BF16,
+    XS_F32,
+    XsError,
+    library_path,
+    load_library,
+    num_partitions,
+    xs_kv_append,
+    xs_last_error,
+    xs_paged_attn_decode,
+    xs_paged_attn_reduce,
+    xs_version,
+)
+from .step import DecodeStep  # noqa: F401

@@ -1,0 +1,186 @@
+"""ctypes binding of libxs.so: argument marshalling only.
+
+Each function takes torch tensors, reads their shapes and device pointers, and calls the C
+function of the same name in libxs.so (declared in include/xs.h). Every step of the
+computation runs in the library's HIP kernels. There is no fallback path: if the library is
+not built, or the library rejects a call, these functions raise.
+
+torch is imported before the library is loaded. libxs.so then binds to the HIP runtime that
+torch already loaded (both carry the soname libamdhip64.so.7), so the library and torch share
+one runtime, one device context and the same streams.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+LIB_NAME = "libxs.so"
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+XS_F32 = 0
+XS_BF16 = 1
+STATUS = {0: "XS_OK", 1: "XS_EINVAL", 2: "XS_EUNSUPPORTED", 3: "XS_ELAUNCH"}
+
+_lock = threading.Lock()
+_lib: Optional[ctypes.CDLL] = None
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+
+SIGNATURES = {
+    "xs_kv_append": [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp],
+    "xs_paged_attn_decode": [_vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _vp,
+                             _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp],
+    "xs_paged_attn_reduce": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp],
+    "xs_last_error": [],
+    "xs_version": [],
+}
+
+
+class XsError(RuntimeError):
+    def __init__(self, func: str, status: int, message: str):
+        super().__init__(f"{func} returned {STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libxs.so once (raises if it is missing: build it with __graft_entry__.build())."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(f"{p} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+        lib = ctypes.CDLL(p)
+        for name, args in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_char_p if name == "xs_last_error" else ctypes.c_int
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def xs_last_error() -> str:
+    return load_library().xs_last_error().decode()
+
+
+def xs_version() -> int:
+    return load_library().xs_version()
+
+
+def _check(func: str, status: int) -> None:
+    if status != 0:
+        raise XsError(func, status, xs_last_error())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return XS_BF16
+    if t.dtype == torch.float32:
+        return XS_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return stream or None
+    return stream.cuda_stream or None
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev(*ts: Optional[torch.Tensor]) -> None:
+    for t in ts:
+        if t is None:
+            continue
+        _need(t.is_cuda, "all tensors must be on the GPU")
+        _need(t.is_contiguous(), "all tensors must be contiguous")
+
+
+def xs_kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 block_tables: torch.Tensor, context_lens: torch.Tensor, stream=None) -> None:
+    """Write each sequence's new K/V row into slot context_lens[b] - 1 of the paged pools."""
+    _dev(k_new, v_new, k_cache, v_cache, block_tables, context_lens)
+    NB, Hkv, BS, D = k_cache.shape
+    B = k_new.shape[0]
+    _need(k_new.shape == (B, Hkv, D) and v_new.shape == (B, Hkv, D), "k_new/v_new must be [batch, Hkv, D]")
+    _need(v_cache.shape == k_cache.shape, "k_cache and v_cache must have the same shape")
+    _need(len({k_new.dtype, v_new.dtype, k_cache.dtype, v_cache.dtype}) == 1, "K/V dtypes differ")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == B,
+          "block_tables must be int32 [batch, max_blocks_per_seq]")
+    _need(context_lens.dtype == torch.int32 and context_lens.shape == (B,), "context_lens must be int32 [batch]")
+    lib = load_library()
+    _check("xs_kv_append", lib.xs_kv_append(
+        _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        B, Hkv, D, BS, block_tables.shape[1], NB, _dtype_code(k_cache), _stream_handle(stream)))
+
+
+def xs_paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                         out: Optional[torch.Tensor] = None, part_o: Optional[torch.Tensor] = None,
+                         part_m: Optional[torch.Tensor] = None, part_l: Optional[torch.Tensor] = None,
+                         partition_size: int = 0, stream=None) -> None:
+    """Decode attention. partition_size == 0 writes `out`; otherwise the split-K partials."""
+    _dev(q, k_cache, v_cache, block_tables, context_lens, out, part_o, part_m, part_l)
+    B, Hq, D = q.shape
+    NB, Hkv, BS, D2 = k_cache.shape
+    _need(D2 == D and v_cache.shape == k_cache.shape, "pool shapes do not match q")
+    _need(len({q.dtype, k_cache.dtype, v_cache.dtype}) == 1, "q and pool dtypes differ")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == B,
+          "block_tables must be int32 [batch, max_blocks_per_seq]")
+    _need(context_lens.dtype == torch.int32 and context_lens.shape == (B,), "context_lens must be int32 [batch]")
+    NP = 0
+    if partition_size > 0:
+        _need(part_o is not None and part_m is not None and part_l is not None, "split-K needs part_o/m/l")
+        NP = part_m.shape[-1]
+        _need(part_o.shape == (B, Hq, NP, D) and part_m.shape == (B, Hq, NP) and part_l.shape == (B, Hq, NP),
+              "partials must be [B, Hq, NP, D], [B, Hq, NP], [B, Hq, NP]")
+        _need(all(t.dtype == torch.float32 for t in (part_o, part_m, part_l)), "partials are float32")
+    else:
+        _need(out is not None and out.shape == (B, Hq, D) and out.dtype == q.dtype, "out must be q-shaped")
+    lib = load_library()
+    _check("xs_paged_attn_decode", lib.xs_paged_attn_decode(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), float(scale), _ptr(out),
+        _ptr(part_o), _ptr(part_m), _ptr(part_l), B, Hq, Hkv, D, BS, block_tables.shape[1], NB,
+        int(partition_size), NP, _dtype_code(q), _stream_handle(stream)))
+
+
+def xs_paged_attn_reduce(part_o: torch.Tensor, part_m: torch.Tensor, part_l: torch.Tensor,
+                         context_lens: torch.Tensor, out: torch.Tensor, partition_size: int, stream=None) -> None:
+    """Log-sum-exp merge of the split-K partials into `out`."""
+    _dev(part_o, part_m, part_l, context_lens, out)
+    B, Hq, NP, D = part_o.shape
+    _need(part_m.shape == (B, Hq, NP) and part_l.shape == (B, Hq, NP), "partial shapes differ")
+    _need(out.shape == (B, Hq, D), "out must be [B, Hq, D]")
+    _need(context_lens.dtype == torch.int32 and context_lens.shape == (B,), "context_lens must be int32 [batch]")
+    lib = load_library()
+    _check("xs_paged_attn_reduce", lib.xs_paged_attn_reduce(
+        _ptr(part_o), _ptr(part_m), _ptr(part_l), _ptr(context_lens), _ptr(out), B, Hq, D,
+        int(partition_size), NP, _dtype_code(out), _stream_handle(stream)))
+
+
+def num_partitions(max_context_len: int, partition_size: int) -> int:
+    """Partition slots the split-K call needs for contexts up to max_context_len."""
+    return max(1, -(-int(max_context_len) // int(partition_size)))

@@ -1,0 +1,151 @@
+// C ABI of libxs.so: host-side argument checks, then one launch per call on the caller's stream.
+// Every check here runs before any HIP call, so a rejected call touches no device state.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "xs.h"
+#include "xs_internal.h"
+
+#define XS_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return XS_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elt_bytes(int dtype) { return dtype == XS_BF16 ? 2 : 4; }
+
+// Checks shared by the append and decode calls. `who` names the entry point in messages.
+int check_pool_args(const char* who, int batch, int num_kv_heads, int head_dim, int block_size,
+                    int max_blocks_per_seq, int num_blocks, int dtype) {
+  if (batch < 0) return fail(XS_EINVAL, "%s: batch = %d < 0", who, batch);
+  if (num_kv_heads < 1) return fail(XS_EINVAL, "%s: num_kv_heads = %d < 1", who, num_kv_heads);
+  if (max_blocks_per_seq < 1) return fail(XS_EINVAL, "%s: max_blocks_per_seq = %d < 1", who, max_blocks_per_seq);
+  if (num_blocks < 1) return fail(XS_EINVAL, "%s: num_blocks = %d < 1", who, num_blocks);
+  if (dtype != XS_F32 && dtype != XS_BF16) return fail(XS_EUNSUPPORTED, "%s: dtype %d is not XS_F32 or XS_BF16", who, dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(XS_EUNSUPPORTED, "%s: head_dim = %d (supported: 64, 128)", who, head_dim);
+  if (block_size != 8 && block_size != 16 && block_size != 32)
+    return fail(XS_EUNSUPPORTED, "%s: block_size = %d (supported: 8, 16, 32)", who, block_size);
+  if ((long long)max_blocks_per_seq * block_size > 0x7fffffffLL)
+    return fail(XS_EINVAL, "%s: max_blocks_per_seq * block_size overflows int32", who);
+  return XS_OK;
+}
+
+int launch_status(const char* who, hipError_t e) {
+  if (e != hipSuccess) return fail(XS_ELAUNCH, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+XS_API const char* xs_last_error(void) { return g_last_error.c_str(); }
+
+XS_API int xs_version(void) { return 100; /* 0.1.0 */ }
+
+XS_API int xs_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                        const int32_t* block_tables, const int32_t* context_lens, int batch, int num_kv_heads,
+                        int head_dim, int block_size, int max_blocks_per_seq, int num_blocks, int dtype,
+                        void* stream) {
+  const char* who = "xs_kv_append";
+  int st = check_pool_args(who, batch, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, dtype);
+  if (st != XS_OK) return st;
+  if (batch == 0) return ok();
+  if (!k_new || !v_new || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(XS_EINVAL, "%s: a required pointer is NULL", who);
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(XS_EINVAL, "%s: k_new, v_new, k_cache and v_cache must be 16-byte aligned", who);
+  if (2LL * batch * num_kv_heads * (head_dim * elt_bytes(dtype) / 16) > 0x7fffffffLL * 256LL)
+    return fail(XS_EINVAL, "%s: batch * num_kv_heads too large", who);
+  (void)hipGetLastError();  // clear a stale error so the status below is this launch's own
+  return launch_status(who, xs::launch_kv_append(k_new, v_new, k_cache, v_cache, block_tables, context_lens, batch,
+                                                 num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                                                 elt_bytes(dtype), static_cast<hipStream_t>(stream)));
+}
+
+XS_API int xs_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, float scale, void* out, float* part_o, float* part_m,
+                                float* part_l, int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                int block_size, int max_blocks_per_seq, int num_blocks, int partition_size,
+                                int max_partitions, int dtype, void* stream) {
+  const char* who = "xs_paged_attn_decode";
+  int st = check_pool_args(who, batch, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, dtype);
+  if (st != XS_OK) return st;
+  if (num_q_heads < 1) return fail(XS_EINVAL, "%s: num_q_heads = %d < 1", who, num_q_heads);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(XS_EINVAL, "%s: num_q_heads = %d is not a multiple of num_kv_heads = %d", who, num_q_heads,
+                num_kv_heads);
+  if (!isfinite(scale)) return fail(XS_EINVAL, "%s: scale is not finite", who);
+  if (partition_size < 0) return fail(XS_EINVAL, "%s: partition_size = %d < 0", who, partition_size);
+  const bool split = partition_size > 0;
+  if (split) {
+    if (partition_size % block_size != 0)
+      return fail(XS_EINVAL, "%s: partition_size = %d is not a multiple of block_size = %d", who, partition_size,
+                  block_size);
+    if (max_partitions < 1) return fail(XS_EINVAL, "%s: max_partitions = %d < 1 with split-K", who, max_partitions);
+  }
+  const int chunks = (num_q_heads / num_kv_heads) / xs::heads_per_chunk(num_q_heads / num_kv_heads);
+  const long long grid = (long long)batch * num_kv_heads * chunks * (split ? max_partitions : 1);
+  if (grid > 0x7fffffffLL) return fail(XS_EINVAL, "%s: %lld work items exceed the launch limit", who, grid);
+  if (batch == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(XS_EINVAL, "%s: a required pointer is NULL", who);
+  if (split) {
+    if (!part_o || !part_m || !part_l)
+      return fail(XS_EINVAL, "%s: split-K (partition_size > 0) needs part_o, part_m and part_l", who);
+    if (!aligned16(part_o)) return fail(XS_EINVAL, "%s: part_o must be 16-byte aligned", who);
+  } else {
+    if (!out) return fail(XS_EINVAL, "%s: out is NULL with partition_size == 0", who);
+    if (part_o || part_m || part_l)
+      return fail(XS_EINVAL, "%s: part_o/part_m/part_l must be NULL when partition_size == 0", who);
+    if (!aligned16(out)) return fail(XS_EINVAL, "%s: out must be 16-byte aligned", who);
+  }
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(XS_EINVAL, "%s: q, k_cache and v_cache must be 16-byte aligned", who);
+  (void)hipGetLastError();
+  return launch_status(who, xs::launch_paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                                                    part_o, part_m, part_l, batch, num_q_heads, num_kv_heads,
+                                                    head_dim, block_size, max_blocks_per_seq, num_blocks,
+                                                    partition_size, max_partitions, dtype == XS_BF16,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
+XS_API int xs_paged_attn_reduce(const float* part_o, const float* part_m, const float* part_l,
+                                const int32_t* context_lens, void* out, int batch, int num_q_heads, int head_dim,
+                                int partition_size, int max_partitions, int dtype, void* stream) {
+  const char* who = "xs_paged_attn_reduce";
+  if (batch < 0) return fail(XS_EINVAL, "%s: batch = %d < 0", who, batch);
+  if (num_q_heads < 1) return fail(XS_EINVAL, "%s: num_q_heads = %d < 1", who, num_q_heads);
+  if (dtype != XS_F32 && dtype != XS_BF16) return fail(XS_EUNSUPPORTED, "%s: dtype %d is not XS_F32 or XS_BF16", who, dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(XS_EUNSUPPORTED, "%s: head_dim = %d (supported: 64, 128)", who, head_dim);
+  if (partition_size < 1) return fail(XS_EINVAL, "%s: partition_size = %d < 1", who, partition_size);
+  if (max_partitions < 1) return fail(XS_EINVAL, "%s: max_partitions = %d < 1", who, max_partitions);
+  if ((long long)batch * num_q_heads > 0x7fffffffLL) return fail(XS_EINVAL, "%s: batch * num_q_heads too large", who);
+  if (batch == 0) return ok();
+  if (!part_o || !part_m || !part_l || !context_lens || !out)
+    return fail(XS_EINVAL, "%s: a required pointer is NULL", who);
+  (void)hipGetLastError();
+  return launch_status(who, xs::launch_paged_reduce(part_o, part_m, part_l, context_lens, out, batch, num_q_heads,
+                                                    head_dim, partition_size, max_partitions, dtype == XS_BF16,
+                                                    static_cast<hipStream_t>(stream)));
+}

@@ -1,0 +1,88 @@
+// Log-sum-exp merge of split-K partitions: one wavefront per (sequence, query head).
+//
+// Partition j holds (o_j, m_j, l_j) with m_j the max scaled score, l_j = sum exp(s - m_j) and
+// o_j the partition's normalised output. With M = max_j m_j and w_j = l_j exp(m_j - M),
+//   out = sum_j w_j o_j / sum_j w_j,
+// which equals the softmax over the whole context (the partitions split its sum). The split
+// and its merge are this library's design for long contexts; the pages have no split.
+#include <math.h>
+
+#include "xs_device.h"
+#include "xs_internal.h"
+
+namespace xs {
+namespace {
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(64) void paged_reduce_kernel(const float* __restrict__ part_o,
+                                                          const float* __restrict__ part_m,
+                                                          const float* __restrict__ part_l,
+                                                          const int32_t* __restrict__ context_lens,
+                                                          void* __restrict__ out, int num_q_heads,
+                                                          int partition_size, int max_partitions) {
+  constexpr int DPL = D / 64;  // output elements per lane
+  const int lane = threadIdx.x;
+  const size_t row = blockIdx.x;  // (b, h)
+  const int b = (int)(row / num_q_heads);
+  const int L = context_lens[b];
+  int n = L > 0 ? (L + partition_size - 1) / partition_size : 0;
+  n = min(n, max_partitions);
+  const float* pm = part_m + row * max_partitions;
+  const float* pl = part_l + row * max_partitions;
+
+  float M = -INFINITY;
+  for (int j = lane; j < n; j += 64) M = fmaxf(M, pm[j]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+
+  float acc[DPL];
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
+  float W = 0.f;
+  if (M != -INFINITY) {
+    const float M2 = M * kLog2e;
+    const float* po = part_o + row * max_partitions * D + (size_t)lane * DPL;
+    for (int j = 0; j < n; ++j) {
+      const float w = pl[j] * fast_exp2(fmaf(pm[j], kLog2e, -M2));
+      W += w;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) acc[k] = fmaf(w, po[(size_t)j * D + k], acc[k]);
+    }
+  }
+  const float inv = W > 0.f ? 1.f / W : 0.f;
+  if constexpr (BF16) {
+    if constexpr (DPL == 2) {
+      reinterpret_cast<uint32_t*>(out)[row * (D / 2) + lane] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    } else {
+      reinterpret_cast<uint16_t*>(out)[row * D + lane] = (uint16_t)f32_to_bf16_rne(acc[0] * inv);
+    }
+  } else {
+    float* o = reinterpret_cast<float*>(out) + row * D + (size_t)lane * DPL;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) o[k] = acc[k] * inv;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_paged_reduce(const float* part_o, const float* part_m, const float* part_l,
+                               const int32_t* context_lens, void* out, int batch, int num_q_heads, int head_dim,
+                               int partition_size, int max_partitions, bool bf16, hipStream_t stream) {
+  const dim3 grid((unsigned)((long long)batch * num_q_heads));
+#define XS_LAUNCH(BF, D_)                                                                                      \
+  hipLaunchKernelGGL((paged_reduce_kernel<BF, D_>), grid, dim3(64), 0, stream, part_o, part_m, part_l,       \
+                     context_lens, out, num_q_heads, partition_size, max_partitions)
+  if (bf16) {
+    if (head_dim == 64) XS_LAUNCH(true, 64);
+    else if (head_dim == 128) XS_LAUNCH(true, 128);
+    else return hipErrorInvalidValue;
+  } else {
+    if (head_dim == 64) XS_LAUNCH(false, 64);
+    else if (head_dim == 128) XS_LAUNCH(false, 128);
+    else return hipErrorInvalidValue;
+  }
+#undef XS_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace xs

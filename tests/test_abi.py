@@ -1,0 +1,135 @@
+"""C ABI checks that need no GPU: the library loads, exports what include/xs.h declares, and
+rejects bad arguments on the host with a status and a message, before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_decode_xs_amd import _binding as xb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "xs.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(xb.LIB_PATH), reason="libxs.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(xs_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("xs_kv_append", "xs_paged_attn_decode", "xs_paged_attn_reduce", "xs_last_error", "xs_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(xb.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in xb.SIGNATURES, f"binding lacks {name}"
+
+
+def test_library_exports_nothing_else():
+    import subprocess
+
+    out = subprocess.run(["nm", "-D", "--defined-only", xb.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert {n for n in exported if n.startswith("xs_")} == set(declared_functions())
+
+
+def test_version():
+    assert xb.load_library().xs_version() >= 100
+
+
+# Calls below are all rejected by the host checks, which run before any HIP call.
+F, B = 0, 1
+FAKE = 1 << 20  # a 16-byte aligned non-null address that is never dereferenced
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, scale=0.125, out=FAKE, po=None, pm=None, pl=None, batch=2,
+             hq=8, hkv=2, d=128, bs=16, mbps=4, nb=16, p=0, np_=0, dt=B, stream=None)
+    a.update(kw)
+    lib = xb.load_library()
+    return lib.xs_paged_attn_decode(a["q"], a["k"], a["v"], a["bt"], a["cl"], a["scale"], a["out"], a["po"], a["pm"],
+                                    a["pl"], a["batch"], a["hq"], a["hkv"], a["d"], a["bs"], a["mbps"], a["nb"],
+                                    a["p"], a["np_"], a["dt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(hq=6, hkv=4), 1, "multiple"),
+    (dict(d=96), 2, "head_dim"),
+    (dict(bs=12), 2, "block_size"),
+    (dict(dt=7), 2, "dtype"),
+    (dict(batch=-1), 1, "batch"),
+    (dict(hkv=0), 1, "num_kv_heads"),
+    (dict(nb=0), 1, "num_blocks"),
+    (dict(q=None), 1, "NULL"),
+    (dict(out=None), 1, "out is NULL"),
+    (dict(p=24, np_=2, po=FAKE, pm=FAKE, pl=FAKE), 1, "multiple of block_size"),
+    (dict(p=32, np_=0, po=FAKE, pm=FAKE, pl=FAKE), 1, "max_partitions"),
+    (dict(p=32, np_=2), 1, "needs part_o"),
+    (dict(po=FAKE), 1, "must be NULL"),
+    (dict(q=FAKE + 4), 1, "aligned"),
+    (dict(scale=float("inf")), 1, "scale"),
+    (dict(p=-16), 1, "partition_size"),
+    (dict(batch=1 << 20, hkv=8, hq=8, p=16, np_=1 << 10, po=FAKE, pm=FAKE, pl=FAKE), 1, "launch limit"),
+])
+def test_decode_rejects(kw, status, needle):
+    assert _decode(**kw) == status
+    assert needle in xb.xs_last_error()
+
+
+def test_empty_batch_is_a_noop():
+    assert _decode(batch=0, q=None, out=None) == 0
+    assert xb.xs_last_error() == ""
+
+
+def _append(**kw):
+    a = dict(kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, batch=2, hkv=2, d=64, bs=16, mbps=4, nb=8, dt=B,
+             stream=None)
+    a.update(kw)
+    return xb.load_library().xs_kv_append(a["kn"], a["vn"], a["kc"], a["vc"], a["bt"], a["cl"], a["batch"], a["hkv"],
+                                          a["d"], a["bs"], a["mbps"], a["nb"], a["dt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(kc=None), 1, "NULL"),
+    (dict(d=80), 2, "head_dim"),
+    (dict(bs=64), 2, "block_size"),
+    (dict(vn=FAKE + 2), 1, "aligned"),
+    (dict(mbps=0), 1, "max_blocks_per_seq"),
+    (dict(dt=-1), 2, "dtype"),
+])
+def test_append_rejects(kw, status, needle):
+    assert _append(**kw) == status
+    assert needle in xb.xs_last_error()
+
+
+def _reduce(**kw):
+    a = dict(po=FAKE, pm=FAKE, pl=FAKE, cl=FAKE, out=FAKE, batch=2, hq=4, d=64, p=16, np_=3, dt=F, stream=None)
+    a.update(kw)
+    return xb.load_library().xs_paged_attn_reduce(a["po"], a["pm"], a["pl"], a["cl"], a["out"], a["batch"], a["hq"],
+                                                  a["d"], a["p"], a["np_"], a["dt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(pm=None), 1, "NULL"),
+    (dict(p=0), 1, "partition_size"),
+    (dict(np_=0), 1, "max_partitions"),
+    (dict(d=32), 2, "head_dim"),
+    (dict(hq=0), 1, "num_q_heads"),
+])
+def test_reduce_rejects(kw, status, needle):
+    assert _reduce(**kw) == status
+    assert needle in xb.xs_last_error()
+
+
+def test_binding_raises_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        xb.load_library(str(tmp_path / "nope.so"))

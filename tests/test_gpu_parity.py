@@ -1,0 +1,142 @@
+"""HIP path against the fp64 oracle, through the C ABI (needs an MI355X).
+
+* all five workloads at full size: the append bit-exact over the whole pool, attention within
+  tolerance unsplit and split-K, and the split partials against the oracle's partition
+  statistics;
+* reduced shapes that span several blocks and partitions with ragged tails, every supported
+  head_dim / block_size / dtype, GQA groups 1..16, L = 0 and L = 1;
+* invariants on the GPU: a block-table permutation gives bitwise the same output, as does a
+  second run; one key returns its V exactly.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from tests.gpu_common import OracleResult, as_f64, check_case, log, run_step
+from workloads.device import case_to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _library():
+    import paged_kv_decode_xs_amd as xs
+
+    xs.load_library()
+    torch.cuda.init()
+    yield
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+@pytest.mark.parametrize("name", wl.ORDER)
+def test_workload_full_size(name):
+    w = wl.WORKLOADS[name]
+    case = wl.make_case(w)
+    ref = OracleResult(case, w.partition_size)
+    err0, _, _ = check_case(case, 0, ref, label=f"{name} unsplit")
+    err1, _, _ = check_case(case, w.partition_size, ref, check_pools=False, label=f"{name} split")
+    log(f"[gpu] {name}: max |err| unsplit {err0:.3g}, split {err1:.3g}")
+
+
+# ---------------------------------------------------------------- reduced shapes and edge cases
+
+SHAPES = [
+    # dtype, Hq, Hkv, D, BS, lens, P
+    ("f32", 12, 12, 64, 16, [32], 16),
+    ("f32", 8, 2, 128, 16, [1, 17, 100, 16], 32),
+    ("f32", 4, 4, 64, 8, [0, 9, 40], 8),
+    ("f32", 6, 2, 64, 32, [65, 3], 32),
+    ("bf16", 12, 12, 64, 16, [64, 1000, 333, 1], 128),
+    ("bf16", 32, 8, 128, 16, [1, 15, 16, 17, 4095, 513], 64),
+    ("bf16", 32, 8, 128, 8, [200, 7], 16),
+    ("bf16", 32, 8, 128, 32, [0, 31, 33, 700], 96),
+    ("bf16", 16, 16, 128, 16, [50, 51], 16),
+    ("bf16", 24, 8, 128, 16, [77, 130], 32),   # group 3: one head per wavefront, 3 chunks
+    ("bf16", 12, 2, 64, 16, [90, 260], 64),    # group 6: two heads per wavefront
+    ("bf16", 16, 2, 128, 16, [300, 45], 64),   # group 8
+    ("bf16", 32, 2, 128, 16, [129, 2], 48),    # group 16: two chunks of 8
+    ("f32", 32, 2, 64, 16, [70, 18], 32),
+]
+
+
+def _shape_case(dtype, Hq, Hkv, D, BS, lens, seed):
+    mbps = max(1, -(-max(lens) // BS) + 1)
+    w = wl.Workload(name="shape", description="", dtype=dtype, batch=len(lens), num_q_heads=Hq,
+                    num_kv_heads=Hkv, head_dim=D, block_size=BS, ctx=("fixed", lens), num_blocks=None,
+                    max_blocks_per_seq=mbps, values="normal", seed=seed, partition_size=BS)
+    return wl.make_case(w)
+
+
+@pytest.mark.parametrize("idx", range(len(SHAPES)))
+def test_shapes(idx):
+    dtype, Hq, Hkv, D, BS, lens, P = SHAPES[idx]
+    case = _shape_case(dtype, Hq, Hkv, D, BS, lens, seed=100 + idx)
+    ref = OracleResult(case, P)
+    check_case(case, 0, ref, label=f"shape{idx} unsplit")
+    check_case(case, P, ref, check_pools=False, label=f"shape{idx} split")
+    # Partition = one block: many partitions per sequence.
+    check_case(case, BS, OracleResult(case, BS), check_pools=False, label=f"shape{idx} P=BS")
+
+
+def test_empty_contexts_give_zeros():
+    case = _shape_case("bf16", 8, 2, 128, 16, [0, 0, 5], seed=7)
+    ref = OracleResult(case, 32)
+    for P in (0, 32):
+        _, step, _ = check_case(case, P, ref, label=f"empty P={P}")
+        assert torch.count_nonzero(step.out[:2]).item() == 0
+
+
+def test_single_key_returns_v_exactly():
+    case = _shape_case("f32", 8, 2, 128, 16, [1, 1], seed=8)
+    _, step, _ = check_case(case, 0, OracleResult(case), label="L=1")
+    got = step.out.cpu().numpy()
+    for b in range(2):
+        for h in range(8):
+            assert np.array_equal(got[b, h], case.v_new[b, h // 4]), (b, h)
+
+
+def test_permutation_and_rerun_are_bitwise_identical():
+    w = wl.WORKLOADS["qwen3_8b_b64"].with_(batch=6, ctx=("uniform", 1, 1500), max_blocks_per_seq=96)
+    case = wl.make_case(w, seed=21)
+    P = 64
+    ref = OracleResult(case, P)
+    _, step1, dev = check_case(case, P, ref, label="perm base")
+    out1 = step1.out.clone()
+    step1.run()
+    torch.cuda.synchronize()
+    assert torch.equal(step1.out.view(torch.int16), out1.view(torch.int16)), "second run differs"
+    # Re-place every block by a permutation of pool ids and rewrite the table.
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(case.num_blocks)
+    case2 = wl.Case(workload=w, q=case.q, k_new=case.k_new, v_new=case.v_new,
+                    k_cache=np.empty_like(case.k_cache), v_cache=np.empty_like(case.v_cache),
+                    block_tables=np.where(case.block_tables >= 0, perm[np.maximum(case.block_tables, 0)], -1)
+                    .astype(np.int32), context_lens=case.context_lens)
+    case2.k_cache[perm] = case.k_cache
+    case2.v_cache[perm] = case.v_cache
+    for P2 in (0, P):
+        dev2 = case_to_device(case2)
+        s2 = run_step(dev2, w.scale, P2, int(case.context_lens.max()))
+        s1 = run_step(case_to_device(case), w.scale, P2, int(case.context_lens.max()))
+        assert torch.equal(s2.out.view(torch.int16), s1.out.view(torch.int16)), f"permutation changed bits (P={P2})"
+    log("[gpu] permutation and rerun: bitwise identical")
+
+
+def test_stream_argument_is_honoured():
+    case = _shape_case("bf16", 32, 8, 128, 16, [300, 1000], seed=9)
+    ref = OracleResult(case, 128)
+    dev = case_to_device(case)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        import paged_kv_decode_xs_amd as xs
+
+        step = xs.DecodeStep(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["context_lens"],
+                             dev["k_new"], dev["v_new"], case.workload.scale, partition_size=128)
+        step.run(stream=s)
+    s.synchronize()
+    from tests.gpu_common import TOL, assert_close
+
+    assert_close(as_f64(step.out), ref.out, *TOL["bf16"], "side stream")
