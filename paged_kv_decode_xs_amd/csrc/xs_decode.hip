@@ -87,9 +87,14 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(
 
   const bool split = part_blocks > 0;
   const int np = split ? max_partitions : 1;
+  // Work items are numbered partition-major. The hardware deals workgroups round-robin to the
+  // eight XCDs, so neighbouring ids must carry similar work: every (sequence, kv head) has a
+  // first partition but only long sequences have late ones, and with the partition index
+  // outermost each XCD gets an even share of every partition depth.
   unsigned wg = blockIdx.x;
-  const int p = wg % np;
-  wg /= np;
+  const unsigned per_p = gridDim.x / (unsigned)np;  // batch * num_kv_heads * chunks
+  const int p = wg / per_p;
+  wg %= per_p;
   const int ch = wg % chunks;
   wg /= chunks;
   const int g = wg % num_kv_heads;
@@ -319,6 +324,10 @@ hipError_t launch_paged_decode(const void* q, const void* k_cache, const void* v
                                float* part_l, int batch, int num_q_heads, int num_kv_heads, int head_dim,
                                int block_size, int max_blocks_per_seq, int num_blocks, int partition_size,
                                int max_partitions, bool bf16, hipStream_t stream) {
+  if (mfma_decode_supported(bf16, head_dim, block_size))
+    return launch_paged_decode_mfma(q, k_cache, v_cache, block_tables, context_lens, scale, out, part_o, part_m,
+                                    part_l, batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                                    max_blocks_per_seq, num_blocks, partition_size, max_partitions, stream);
   const int gc = heads_per_chunk(num_q_heads / num_kv_heads);
 #define XS_ARGS                                                                                                 \
   block_size, gc, q, k_cache, v_cache, block_tables, context_lens, scale, out, part_o, part_m, part_l, batch, \

@@ -29,7 +29,9 @@ __global__ __launch_bounds__(64) void paged_reduce_kernel(const float* __restric
   n = min(n, max_partitions);
   const float* pm = part_m + row * max_partitions;
   const float* pl = part_l + row * max_partitions;
+  const float* po = part_o + row * max_partitions * D + (size_t)lane * DPL;
 
+  // Lane j holds partition j (64 at a time): its max, then its weight l_j 2^((m_j - M) log2e).
   float M = -INFINITY;
   for (int j = lane; j < n; j += 64) M = fmaxf(M, pm[j]);
 #pragma unroll
@@ -41,14 +43,36 @@ __global__ __launch_bounds__(64) void paged_reduce_kernel(const float* __restric
   float W = 0.f;
   if (M != -INFINITY) {
     const float M2 = M * kLog2e;
-    const float* po = part_o + row * max_partitions * D + (size_t)lane * DPL;
-    for (int j = 0; j < n; ++j) {
-      const float w = pl[j] * fast_exp2(fmaf(pm[j], kLog2e, -M2));
+    for (int base = 0; base < n; base += 64) {
+      const int jj = base + lane;
+      const float w = jj < n ? pl[jj] * fast_exp2(fmaf(pm[jj], kLog2e, -M2)) : 0.f;
       W += w;
+      const int cnt = min(64, n - base);
+      int k = 0;
+      // Eight partitions per round so that their loads are in flight together.
+      for (; k + 8 <= cnt; k += 8) {
+        float o[8][DPL];
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) acc[k] = fmaf(w, po[(size_t)j * D + k], acc[k]);
+        for (int u = 0; u < 8; ++u) {
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) o[u][e] = po[(size_t)(base + k + u) * D + e];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k + u));
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) acc[e] = fmaf(wk, o[u][e], acc[e]);
+        }
+      }
+      for (; k < cnt; ++k) {
+        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[e] = fmaf(wk, po[(size_t)(base + k) * D + e], acc[e]);
+      }
     }
   }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) W += __shfl_xor(W, off, 64);
   const float inv = W > 0.f ? 1.f / W : 0.f;
   if constexpr (BF16) {
     if constexpr (DPL == 2) {

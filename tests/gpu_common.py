@@ -14,8 +14,12 @@ from workloads.device import case_to_device, to_numpy_bits
 
 # Tolerances: fp32 1e-5 absolute; bf16 2e-2 absolute + 2e-2 relative, elementwise against the fp64 oracle.
 TOL = {"f32": (1e-5, 0.0), "bf16": (2e-2, 2e-2)}
-# fp32 partials of the split path (exact bf16/fp32 inputs, fp32 arithmetic): a much tighter check.
+# fp32 partials of the split path (exact bf16/fp32 inputs, fp32 arithmetic): a much tighter check
+# than the output bar. For bf16 pools the matrix-core PV rounds the weights p to bf16 (relative
+# error <= 2^-9), so o_j = sum p V / l can move by up to 2^-9 * max|V|; that bound is added to
+# part_o's tolerance. m_j and l_j come from unrounded fp32 weights and keep the tight bound.
 PART_TOL = (5e-5, 1e-5)
+P_BF16_REL = 2.0 ** -9
 
 
 def log(msg: str) -> None:
@@ -87,6 +91,10 @@ def check_partials(step, ref: OracleResult, case) -> None:
     pm = step.part_m.cpu().double().numpy()
     pl = step.part_l.cpu().double().numpy()
     atol, rtol = PART_TOL
+    atol_o = atol
+    if case.workload.dtype == "bf16":
+        vmax = float(np.nanmax(np.abs(oracle.decode_values(ref.v_pool, "bf16"))))
+        atol_o = atol + P_BF16_REL * vmax
     for b in range(case.workload.batch):
         for h in range(case.workload.num_q_heads):
             o, m, l = ref.stats[b][h]
@@ -95,4 +103,4 @@ def check_partials(step, ref: OracleResult, case) -> None:
                 continue
             assert_close(pm[b, h, :n], m, atol, rtol, f"part_m[{b},{h}]")
             assert_close(pl[b, h, :n], l, atol, 1e-5, f"part_l[{b},{h}]")
-            assert_close(po[b, h, :n], o, atol, rtol, f"part_o[{b},{h}]")
+            assert_close(po[b, h, :n], o, atol_o, rtol, f"part_o[{b},{h}]")
