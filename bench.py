@@ -4,10 +4,11 @@
 
 Prints ONE JSON line on stdout (diagnostics go to stderr):
   value         K+V bytes the step must stream / measured step time, in GB/s (whole job, 1 GPU)
-  ms_per_step   mean wall time of one step on the GPU (HIP events around K back-to-back steps)
+  ms_per_step   mean time of one step on the GPU (HIP events around K back-to-back steps)
   seqs_per_s    batch / step time
   roofline      the decode kernel alone: its algorithmic bytes per launch / its mean duration
-                (HIP events around each decode launch, on the launch stream) vs 8 TB/s;
+                (HIP events around each decode launch, on the launch stream, in a second pass
+                of the same K steps) vs 8 TB/s;
                 `traffic` comes from the rocprofv3 FETCH_SIZE/WRITE_SIZE summary committed
                 in profiles/, and is null when the kernel source changed since it was taken
   cpu_baseline  the fp64 oracle timed on the host over a bounded sample of the same workload;
@@ -52,7 +53,7 @@ def decode_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str, partition: int):
+def read_traffic(workload: str, partition: int, fused: bool):
     """Per-launch HBM bytes of the decode kernel from the committed rocprofv3 counter summary."""
     path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.txt")
     if not os.path.exists(path):
@@ -63,7 +64,8 @@ def read_traffic(workload: str, partition: int):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("decode_source_sha256") != decode_source_hash() or kv.get("partition_size") != str(partition):
+    if (kv.get("decode_source_sha256") != decode_source_hash() or kv.get("partition_size") != str(partition)
+            or kv.get("fused") != str(fused)):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -145,6 +147,8 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=None, help="pool copies to rotate through")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fuse", action="store_true",
+                    help="issue xs_kv_append and xs_paged_attn_decode separately instead of the fused call")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -176,36 +180,57 @@ def main() -> int:
     pools = [(dev["k_cache"], dev["v_cache"])] + [(dev["k_cache"].clone(), dev["v_cache"].clone())
                                                    for _ in range(R - 1)]
     maxlen = int(case.context_lens.max())
+    fused = not args.no_fuse
     steps = [xs.DecodeStep(dev["q"], kc, vc, dev["block_tables"], dev["context_lens"], dev["k_new"], dev["v_new"],
-                           w.scale, partition_size=P, max_context_len=maxlen) for kc, vc in pools]
+                           w.scale, partition_size=P, max_context_len=maxlen, fused=fused) for kc, vc in pools]
     stream = torch.cuda.current_stream()
     for i in range(args.warmup):
         steps[i % R].run(stream)
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+
+    def one_step(i, ev=None):
+        s = steps[i % R]
+        if fused:
+            if ev is not None:
+                ev[0].record(stream)
+            s.append_and_attend(stream)
+        else:
+            s.append(stream)
+            if ev is not None:
+                ev[0].record(stream)
+            s.attend(stream)
+        if ev is not None:
+            ev[1].record(stream)
+        s.reduce(stream)
+
+    # Timed region: exactly K steps, no other work or events between them.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(K):
-        s = steps[i % R]
-        s.append(stream)
-        ev[i][0].record(stream)
-        s.attend(stream)
-        ev[i][1].record(stream)
-        s.reduce(stream)
+        one_step(i)
     end.record(stream)
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / K
+
+    # The decode kernel alone: the same K steps again, with HIP events around each decode launch on
+    # its stream (events between launches add a few microseconds of GPU time, so they stay out of
+    # the timed region above).
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        one_step(i, ev[i])
+    torch.cuda.synchronize()
     decode_ms = [a.elapsed_time(b) for a, b in ev]
     decode_ms_mean = float(np.mean(decode_ms))
 
     ab = algorithmic_bytes(case, P)
     kv_gbs = ab["kv"] / (ms_step * 1e-3) / 1e9
-    achieved = ab["decode"] / (decode_ms_mean * 1e-3) / 1e9
-    traffic = read_traffic(w.name, P)
+    decode_bytes = ab["decode"] + (ab["append"] if fused else 0)
+    achieved = decode_bytes / (decode_ms_mean * 1e-3) / 1e9
+    traffic = read_traffic(w.name, P, fused)
     result = {
         "metric": METRIC,
         "value": round(kv_gbs, 2),
@@ -230,7 +255,8 @@ def main() -> int:
             "partition_size": P,
             "pool_copies_rotated": R,
             "kv_bytes_per_step": ab["kv"],
-            "step": "kv_append + paged_attn_decode + paged_attn_reduce",
+            "step": ("paged_attn_decode_append (fused append + decode) + paged_attn_reduce" if fused
+                     else "kv_append + paged_attn_decode + paged_attn_reduce"),
         },
         "seqs_per_s": round(w.batch / (ms_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100 * kv_gbs / HBM_PEAK_GBS, 2),
@@ -241,8 +267,8 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "paged_decode_kernel",
-            "algorithmic_bytes_per_launch": ab["decode"],
+            "kernel": "paged_decode_mfma_kernel" + (" (fused append)" if fused else ""),
+            "algorithmic_bytes_per_launch": decode_bytes,
             "mean_launch_us": round(decode_ms_mean * 1e3, 2),
         },
     }

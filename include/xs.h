@@ -112,6 +112,27 @@ int xs_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache
                          int partition_size, int max_partitions, int dtype, void* stream);
 
 /*
+ * xs_kv_append followed by xs_paged_attn_decode, in one launch (the decode step without the
+ * append's separate kernel). Same arguments as xs_paged_attn_decode plus k_new, v_new
+ * [batch, num_kv_heads, head_dim] (read), and the pools are written: for each sequence with
+ * 1 <= L_b <= max_blocks_per_seq * block_size, row (block_tables[b, (L_b-1) / block_size], g,
+ * (L_b-1) % block_size, :) of k_cache/v_cache becomes k_new[b, g, :] / v_new[b, g, :], as in
+ * xs_kv_append. The attention result is bit-identical to the two separate calls: the kernel
+ * takes token L_b - 1 straight from k_new/v_new, which are the bits the append stores.
+ * Sources: the batched append and the decode attention of xserv compare phase10...cf1e9e41,
+ * attention.rs (`reshape_and_cache_batched_bf16`, `paged_decode_attention`), issued back to
+ * back by the decode step.
+ */
+int xs_paged_attn_decode_append(const void* q, const void* k_new, const void* v_new,
+                                void* k_cache, void* v_cache,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                float scale, void* out,
+                                float* part_o, float* part_m, float* part_l,
+                                int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                int block_size, int max_blocks_per_seq, int num_blocks,
+                                int partition_size, int max_partitions, int dtype, void* stream);
+
+/*
  * Log-sum-exp merge of split-K partitions (not on the pages: the exact identity of the
  * unsplit softmax). For each (b, h), with n = min(ceil(L_b / P), max_partitions),
  *   M = max_j m_j,  w_j = l_j exp(m_j - M),  out[b, h, :] = sum_j w_j o_j / sum_j w_j.

@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     xs_kv_append,
     xs_last_error,
     xs_paged_attn_decode,
+    xs_paged_attn_decode_append,
     xs_paged_attn_reduce,
     xs_version,
 )

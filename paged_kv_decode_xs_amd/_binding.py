@@ -37,6 +37,8 @@ SIGNATURES = {
     "xs_kv_append": [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp],
     "xs_paged_attn_decode": [_vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _vp,
                              _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp],
+    "xs_paged_attn_decode_append": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _vp,
+                                    _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp],
     "xs_paged_attn_reduce": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp],
     "xs_last_error": [],
     "xs_version": [],
@@ -137,12 +139,7 @@ def xs_kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor
         B, Hkv, D, BS, block_tables.shape[1], NB, _dtype_code(k_cache), _stream_handle(stream)))
 
 
-def xs_paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                         block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
-                         out: Optional[torch.Tensor] = None, part_o: Optional[torch.Tensor] = None,
-                         part_m: Optional[torch.Tensor] = None, part_l: Optional[torch.Tensor] = None,
-                         partition_size: int = 0, stream=None) -> None:
-    """Decode attention. partition_size == 0 writes `out`; otherwise the split-K partials."""
+def _decode_common(q, k_cache, v_cache, block_tables, context_lens, out, part_o, part_m, part_l, partition_size):
     _dev(q, k_cache, v_cache, block_tables, context_lens, out, part_o, part_m, part_l)
     B, Hq, D = q.shape
     NB, Hkv, BS, D2 = k_cache.shape
@@ -160,11 +157,40 @@ def xs_paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
         _need(all(t.dtype == torch.float32 for t in (part_o, part_m, part_l)), "partials are float32")
     else:
         _need(out is not None and out.shape == (B, Hq, D) and out.dtype == q.dtype, "out must be q-shaped")
+    return B, Hq, Hkv, D, BS, NB, NP
+
+
+def xs_paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                         out: Optional[torch.Tensor] = None, part_o: Optional[torch.Tensor] = None,
+                         part_m: Optional[torch.Tensor] = None, part_l: Optional[torch.Tensor] = None,
+                         partition_size: int = 0, stream=None) -> None:
+    """Decode attention. partition_size == 0 writes `out`; otherwise the split-K partials."""
+    B, Hq, Hkv, D, BS, NB, NP = _decode_common(q, k_cache, v_cache, block_tables, context_lens, out, part_o,
+                                               part_m, part_l, partition_size)
     lib = load_library()
     _check("xs_paged_attn_decode", lib.xs_paged_attn_decode(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), float(scale), _ptr(out),
         _ptr(part_o), _ptr(part_m), _ptr(part_l), B, Hq, Hkv, D, BS, block_tables.shape[1], NB,
         int(partition_size), NP, _dtype_code(q), _stream_handle(stream)))
+
+
+def xs_paged_attn_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+                                v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                scale: float, out: Optional[torch.Tensor] = None,
+                                part_o: Optional[torch.Tensor] = None, part_m: Optional[torch.Tensor] = None,
+                                part_l: Optional[torch.Tensor] = None, partition_size: int = 0, stream=None) -> None:
+    """The KV append and the decode attention in one launch (same results as the two calls)."""
+    B, Hq, Hkv, D, BS, NB, NP = _decode_common(q, k_cache, v_cache, block_tables, context_lens, out, part_o,
+                                               part_m, part_l, partition_size)
+    _dev(k_new, v_new)
+    _need(k_new.shape == (B, Hkv, D) and v_new.shape == (B, Hkv, D), "k_new/v_new must be [batch, Hkv, D]")
+    _need(k_new.dtype == q.dtype and v_new.dtype == q.dtype, "k_new/v_new dtype differs from q")
+    lib = load_library()
+    _check("xs_paged_attn_decode_append", lib.xs_paged_attn_decode_append(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        float(scale), _ptr(out), _ptr(part_o), _ptr(part_m), _ptr(part_l), B, Hq, Hkv, D, BS,
+        block_tables.shape[1], NB, int(partition_size), NP, _dtype_code(q), _stream_handle(stream)))
 
 
 def xs_paged_attn_reduce(part_o: torch.Tensor, part_m: torch.Tensor, part_l: torch.Tensor,

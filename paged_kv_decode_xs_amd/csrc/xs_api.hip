@@ -82,51 +82,115 @@ XS_API int xs_kv_append(const void* k_new, const void* v_new, void* k_cache, voi
                                                  elt_bytes(dtype), static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+// Checks of a decode call (fused or not). Returns XS_OK, or the status of the first violation.
+int check_decode(const char* who, const xs::DecodeArgs& a, int dtype) {
+  int st = check_pool_args(who, a.batch, a.num_kv_heads, a.head_dim, a.block_size, a.max_blocks_per_seq,
+                           a.num_blocks, dtype);
+  if (st != XS_OK) return st;
+  if (a.num_q_heads < 1) return fail(XS_EINVAL, "%s: num_q_heads = %d < 1", who, a.num_q_heads);
+  if (a.num_q_heads % a.num_kv_heads != 0)
+    return fail(XS_EINVAL, "%s: num_q_heads = %d is not a multiple of num_kv_heads = %d", who, a.num_q_heads,
+                a.num_kv_heads);
+  if (!isfinite(a.scale)) return fail(XS_EINVAL, "%s: scale is not finite", who);
+  if (a.partition_size < 0) return fail(XS_EINVAL, "%s: partition_size = %d < 0", who, a.partition_size);
+  const bool split = a.partition_size > 0;
+  if (split) {
+    if (a.partition_size % a.block_size != 0)
+      return fail(XS_EINVAL, "%s: partition_size = %d is not a multiple of block_size = %d", who, a.partition_size,
+                  a.block_size);
+    if (a.max_partitions < 1)
+      return fail(XS_EINVAL, "%s: max_partitions = %d < 1 with split-K", who, a.max_partitions);
+  }
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const int chunks = group / xs::heads_per_chunk(group);
+  const long long grid = (long long)a.batch * a.num_kv_heads * chunks * (split ? a.max_partitions : 1);
+  if (grid > 0x7fffffffLL) return fail(XS_EINVAL, "%s: %lld work items exceed the launch limit", who, grid);
+  if (a.batch == 0) return XS_OK;
+  if (!a.q || !a.k_cache || !a.v_cache || !a.block_tables || !a.context_lens)
+    return fail(XS_EINVAL, "%s: a required pointer is NULL", who);
+  if (split) {
+    if (!a.part_o || !a.part_m || !a.part_l)
+      return fail(XS_EINVAL, "%s: split-K (partition_size > 0) needs part_o, part_m and part_l", who);
+    if (!aligned16(a.part_o)) return fail(XS_EINVAL, "%s: part_o must be 16-byte aligned", who);
+  } else {
+    if (!a.out) return fail(XS_EINVAL, "%s: out is NULL with partition_size == 0", who);
+    if (a.part_o || a.part_m || a.part_l)
+      return fail(XS_EINVAL, "%s: part_o/part_m/part_l must be NULL when partition_size == 0", who);
+    if (!aligned16(a.out)) return fail(XS_EINVAL, "%s: out must be 16-byte aligned", who);
+  }
+  if (!aligned16(a.q) || !aligned16(a.k_cache) || !aligned16(a.v_cache))
+    return fail(XS_EINVAL, "%s: q, k_cache and v_cache must be 16-byte aligned", who);
+  return XS_OK;
+}
+
+xs::DecodeArgs decode_args(const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                           const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                           float scale, void* out, float* part_o, float* part_m, float* part_l, int batch,
+                           int num_q_heads, int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                           int num_blocks, int partition_size, int max_partitions, int dtype) {
+  xs::DecodeArgs a;
+  a.q = q;
+  a.k_cache = const_cast<void*>(k_cache);
+  a.v_cache = const_cast<void*>(v_cache);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.scale = scale;
+  a.out = out;
+  a.part_o = part_o;
+  a.part_m = part_m;
+  a.part_l = part_l;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.partition_size = partition_size;
+  a.max_partitions = partition_size > 0 ? max_partitions : 1;
+  a.bf16 = dtype == XS_BF16;
+  return a;
+}
+
+}  // namespace
+
 XS_API int xs_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                                 const int32_t* context_lens, float scale, void* out, float* part_o, float* part_m,
                                 float* part_l, int batch, int num_q_heads, int num_kv_heads, int head_dim,
                                 int block_size, int max_blocks_per_seq, int num_blocks, int partition_size,
                                 int max_partitions, int dtype, void* stream) {
   const char* who = "xs_paged_attn_decode";
-  int st = check_pool_args(who, batch, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, dtype);
+  const xs::DecodeArgs a = decode_args(q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens, scale, out,
+                                       part_o, part_m, part_l, batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                                       max_blocks_per_seq, num_blocks, partition_size, max_partitions, dtype);
+  const int st = check_decode(who, a, dtype);
   if (st != XS_OK) return st;
-  if (num_q_heads < 1) return fail(XS_EINVAL, "%s: num_q_heads = %d < 1", who, num_q_heads);
-  if (num_q_heads % num_kv_heads != 0)
-    return fail(XS_EINVAL, "%s: num_q_heads = %d is not a multiple of num_kv_heads = %d", who, num_q_heads,
-                num_kv_heads);
-  if (!isfinite(scale)) return fail(XS_EINVAL, "%s: scale is not finite", who);
-  if (partition_size < 0) return fail(XS_EINVAL, "%s: partition_size = %d < 0", who, partition_size);
-  const bool split = partition_size > 0;
-  if (split) {
-    if (partition_size % block_size != 0)
-      return fail(XS_EINVAL, "%s: partition_size = %d is not a multiple of block_size = %d", who, partition_size,
-                  block_size);
-    if (max_partitions < 1) return fail(XS_EINVAL, "%s: max_partitions = %d < 1 with split-K", who, max_partitions);
-  }
-  const int chunks = (num_q_heads / num_kv_heads) / xs::heads_per_chunk(num_q_heads / num_kv_heads);
-  const long long grid = (long long)batch * num_kv_heads * chunks * (split ? max_partitions : 1);
-  if (grid > 0x7fffffffLL) return fail(XS_EINVAL, "%s: %lld work items exceed the launch limit", who, grid);
   if (batch == 0) return ok();
-  if (!q || !k_cache || !v_cache || !block_tables || !context_lens)
-    return fail(XS_EINVAL, "%s: a required pointer is NULL", who);
-  if (split) {
-    if (!part_o || !part_m || !part_l)
-      return fail(XS_EINVAL, "%s: split-K (partition_size > 0) needs part_o, part_m and part_l", who);
-    if (!aligned16(part_o)) return fail(XS_EINVAL, "%s: part_o must be 16-byte aligned", who);
-  } else {
-    if (!out) return fail(XS_EINVAL, "%s: out is NULL with partition_size == 0", who);
-    if (part_o || part_m || part_l)
-      return fail(XS_EINVAL, "%s: part_o/part_m/part_l must be NULL when partition_size == 0", who);
-    if (!aligned16(out)) return fail(XS_EINVAL, "%s: out must be 16-byte aligned", who);
-  }
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
-    return fail(XS_EINVAL, "%s: q, k_cache and v_cache must be 16-byte aligned", who);
   (void)hipGetLastError();
-  return launch_status(who, xs::launch_paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out,
-                                                    part_o, part_m, part_l, batch, num_q_heads, num_kv_heads,
-                                                    head_dim, block_size, max_blocks_per_seq, num_blocks,
-                                                    partition_size, max_partitions, dtype == XS_BF16,
-                                                    static_cast<hipStream_t>(stream)));
+  return launch_status(who, xs::launch_paged_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+XS_API int xs_paged_attn_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                       void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                                       float scale, void* out, float* part_o, float* part_m, float* part_l, int batch,
+                                       int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                       int max_blocks_per_seq, int num_blocks, int partition_size, int max_partitions,
+                                       int dtype, void* stream) {
+  const char* who = "xs_paged_attn_decode_append";
+  const xs::DecodeArgs a = decode_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out,
+                                       part_o, part_m, part_l, batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                                       max_blocks_per_seq, num_blocks, partition_size, max_partitions, dtype);
+  const int st = check_decode(who, a, dtype);
+  if (st != XS_OK) return st;
+  if (batch == 0) return ok();
+  if (!k_new || !v_new) return fail(XS_EINVAL, "%s: k_new and v_new must not be NULL", who);
+  if (!aligned16(k_new) || !aligned16(v_new)) return fail(XS_EINVAL, "%s: k_new and v_new must be 16-byte aligned", who);
+  (void)hipGetLastError();
+  return launch_status(who, xs::launch_paged_decode(a, static_cast<hipStream_t>(stream)));
 }
 
 XS_API int xs_paged_attn_reduce(const float* part_o, const float* part_m, const float* part_l,

@@ -22,6 +22,8 @@
 // The next block's K and V are loaded while the current block is processed.
 #include <math.h>
 
+#include <atomic>
+
 #include "xs_device.h"
 #include "xs_internal.h"
 
@@ -71,12 +73,7 @@ __device__ __forceinline__ float piece_dot(const uint4& q, const uint4& k) {
 }
 
 template <bool BF16, int D, int BS, int GC>
-__global__ __launch_bounds__(64) void paged_decode_kernel(
-    const uint4* __restrict__ q, const uint4* __restrict__ k_cache, const uint4* __restrict__ v_cache,
-    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens, float scale_log2e,
-    void* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_m, float* __restrict__ part_l,
-    int num_q_heads, int num_kv_heads, int group, int chunks, int max_blocks_per_seq, int num_blocks,
-    int part_blocks, int max_partitions) {
+__global__ __launch_bounds__(64) void paged_decode_kernel(const DecodeParams prm) {
   using Gm = Geo<BF16, D, BS>;
   constexpr int EPL = Gm::kEPL, LPT = Gm::kLPT, TPI = Gm::kTPI, NI = Gm::kNI;
   constexpr float kNegInf = -INFINITY;
@@ -85,8 +82,9 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(
   const int row = lane / LPT;
   const int col = lane % LPT;
 
-  const bool split = part_blocks > 0;
-  const int np = split ? max_partitions : 1;
+  const int num_kv_heads = prm.num_kv_heads;
+  const bool split = prm.part_blocks > 0;
+  const int np = split ? prm.max_partitions : 1;
   // Work items are numbered partition-major. The hardware deals workgroups round-robin to the
   // eight XCDs, so neighbouring ids must carry similar work: every (sequence, kv head) has a
   // first partition but only long sequences have late ones, and with the partition index
@@ -95,34 +93,52 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(
   const unsigned per_p = gridDim.x / (unsigned)np;  // batch * num_kv_heads * chunks
   const int p = wg / per_p;
   wg %= per_p;
-  const int ch = wg % chunks;
-  wg /= chunks;
+  const int ch = wg % prm.chunks;
+  wg /= prm.chunks;
   const int g = wg % num_kv_heads;
   const int b = wg / num_kv_heads;
-  const int h0 = g * group + ch * GC;
+  const int h0 = g * prm.group + ch * GC;
 
-  int L = context_lens[b];
-  L = min(L, max_blocks_per_seq * BS);
+  const int L_in = prm.context_lens[b];
+  const int L = min(L_in, prm.max_blocks_per_seq * BS);
   const int nblk_seq = L > 0 ? (L + BS - 1) / BS : 0;
   int jb = 0, je = nblk_seq;
   if (split) {
-    jb = p * part_blocks;
-    je = min(jb + part_blocks, nblk_seq);
+    jb = p * prm.part_blocks;
+    je = min(jb + prm.part_blocks, nblk_seq);
     if (jb >= je) return;  // partition past the end of this sequence
   }
 
-  const size_t q_row0 = (size_t)b * num_q_heads + h0;
+  const size_t q_row0 = (size_t)b * prm.num_q_heads + h0;
   if (jb >= je) {  // no split and an empty context: the output is zero
     if (row == 0) {
 #pragma unroll
-      for (int h = 0; h < GC; ++h) reinterpret_cast<uint4*>(out)[(q_row0 + h) * LPT + col] = make_uint4(0, 0, 0, 0);
+      for (int h = 0; h < GC; ++h)
+        reinterpret_cast<uint4*>(prm.out)[(q_row0 + h) * LPT + col] = make_uint4(0, 0, 0, 0);
     }
     return;
+  }
+  const int32_t* bt = prm.block_tables + (size_t)b * prm.max_blocks_per_seq;
+  auto valid = [&](int blk) { return blk >= 0 && blk < prm.num_blocks; };
+
+  // Fused append: token L-1 comes from k_new/v_new; the item holding it writes them to the pools.
+  const bool append = prm.k_new != nullptr && L_in >= 1 && L_in == L;
+  const int last = append ? L - 1 : -1;
+  const size_t new_row = ((size_t)b * num_kv_heads + g) * LPT;  // LPT 16-byte pieces per row
+  if (append && ch == 0 && last / BS >= jb && last / BS < je && lane < 2 * LPT) {
+    const int blk = bt[last / BS];
+    if (valid(blk)) {
+      const size_t dst = (((size_t)blk * num_kv_heads + g) * BS + last % BS) * LPT;
+      if (lane < LPT)
+        prm.k_cache_w[dst + lane] = prm.k_new[new_row + lane];
+      else
+        prm.v_cache_w[dst + lane - LPT] = prm.v_new[new_row + lane - LPT];
+    }
   }
 
   uint4 qv[GC];
 #pragma unroll
-  for (int h = 0; h < GC; ++h) qv[h] = q[(q_row0 + h) * LPT + col];
+  for (int h = 0; h < GC; ++h) qv[h] = prm.q[(q_row0 + h) * LPT + col];
 
   float m[GC], l[GC], acc[GC][EPL];
 #pragma unroll
@@ -133,15 +149,16 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
 
-  const int32_t* bt = block_tables + (size_t)b * max_blocks_per_seq;
   const size_t chunk_stride = (size_t)NI * 64;  // uint4 pieces per (block, kv head) chunk
 
-  auto load_chunk = [&](int blk, uint4 (&kr)[NI], uint4 (&vr)[NI]) {
+  auto load_chunk = [&](int blk, int jblk, uint4 (&kr)[NI], uint4 (&vr)[NI]) {
     const size_t base = ((size_t)blk * num_kv_heads + g) * chunk_stride + lane;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) kr[i] = k_cache[base + i * 64];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) vr[i] = v_cache[base + i * 64];
+    for (int i = 0; i < NI; ++i) {
+      const bool is_new = jblk * BS + i * TPI + row == last;
+      kr[i] = load_stream(is_new ? prm.k_new + new_row + col : prm.k_cache + base + i * 64);
+      vr[i] = load_stream(is_new ? prm.v_new + new_row + col : prm.v_cache + base + i * 64);
+    }
   };
 
   auto process = [&](const uint4 (&kr)[NI], const uint4 (&vr)[NI], int nvalid) {
@@ -149,7 +166,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
 #pragma unroll
-      for (int h = 0; h < GC; ++h) s[i][h] = group_sum<LPT>(piece_dot<BF16>(qv[h], kr[i])) * scale_log2e;
+      for (int h = 0; h < GC; ++h) s[i][h] = group_sum<LPT>(piece_dot<BF16>(qv[h], kr[i])) * prm.scale_log2e;
     }
     float v[NI][EPL];
 #pragma unroll
@@ -193,16 +210,16 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(
     const int ids = lane < n ? bt[base + lane] : -1;
     uint4 kr[NI], vr[NI];
     int blk = __builtin_amdgcn_readfirstlane(ids);
-    bool ok = blk >= 0 && blk < num_blocks;
-    if (ok) load_chunk(blk, kr, vr);
+    bool ok = valid(blk);
+    if (ok) load_chunk(blk, base, kr, vr);
     for (int jj = 0; jj < n; ++jj) {
       uint4 kn[NI], vn[NI];
       int blkn = -1;
       bool okn = false;
       if (jj + 1 < n) {
         blkn = __builtin_amdgcn_readlane(ids, jj + 1);
-        okn = blkn >= 0 && blkn < num_blocks;
-        if (okn) load_chunk(blkn, kn, vn);
+        okn = valid(blkn);
+        if (okn) load_chunk(blkn, base + jj + 1, kn, vn);
       }
       if (ok) {
         const int nvalid = min(BS, L - (base + jj) * BS);
@@ -247,13 +264,13 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[e] = acc[h][e] * inv;
     if (split) {
-      const size_t prow = (q_row0 + h) * (size_t)max_partitions + p;
-      float4* po = reinterpret_cast<float4*>(part_o + prow * D + (size_t)col * EPL);
+      const size_t prow = (q_row0 + h) * (size_t)prm.max_partitions + p;
+      float4* po = reinterpret_cast<float4*>(prm.part_o + prow * D + (size_t)col * EPL);
 #pragma unroll
       for (int e = 0; e < EPL; e += 4) po[e / 4] = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
       if (col == 0) {
-        part_m[prow] = m[h] == kNegInf ? kNegInf : m[h] * kLn2;
-        part_l[prow] = l[h];
+        prm.part_m[prow] = m[h] == kNegInf ? kNegInf : m[h] * kLn2;
+        prm.part_l[prow] = l[h];
       }
     } else {
       uint4 w;
@@ -263,50 +280,37 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(
       } else {
         w = make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3]));
       }
-      reinterpret_cast<uint4*>(out)[(q_row0 + h) * LPT + col] = w;
+      reinterpret_cast<uint4*>(prm.out)[(q_row0 + h) * LPT + col] = w;
     }
   }
 }
 
 template <bool BF16, int D, int BS, int GC>
-hipError_t launch_t(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                    const int32_t* context_lens, float scale, void* out, float* part_o, float* part_m,
-                    float* part_l, int batch, int num_q_heads, int num_kv_heads, int max_blocks_per_seq,
-                    int num_blocks, int partition_size, int max_partitions, hipStream_t stream) {
-  const int group = num_q_heads / num_kv_heads;
-  const int chunks = group / GC;
-  const int part_blocks = partition_size > 0 ? partition_size / BS : 0;
-  const long long np = part_blocks > 0 ? max_partitions : 1;
-  const long long grid = (long long)batch * num_kv_heads * chunks * np;
-  hipLaunchKernelGGL((paged_decode_kernel<BF16, D, BS, GC>), dim3((unsigned)grid), dim3(64), 0, stream,
-                     static_cast<const uint4*>(q), static_cast<const uint4*>(k_cache),
-                     static_cast<const uint4*>(v_cache), block_tables, context_lens, scale * kLog2e, out, part_o,
-                     part_m, part_l, num_q_heads, num_kv_heads, group, chunks, max_blocks_per_seq, num_blocks,
-                     part_blocks, max_partitions);
+hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+  const DecodeParams prm = make_params(a, GC);
+  const long long np = prm.part_blocks > 0 ? a.max_partitions : 1;
+  const long long grid = (long long)a.batch * a.num_kv_heads * prm.chunks * np;
+  hipLaunchKernelGGL((paged_decode_kernel<BF16, D, BS, GC>), dim3((unsigned)grid), dim3(64), 0, stream, prm);
   return hipGetLastError();
 }
 
 template <bool BF16, int D, int BS>
-hipError_t launch_gc(int gc, const void* q, const void* kc, const void* vc, const int32_t* bt, const int32_t* cl,
-                     float scale, void* out, float* po, float* pm, float* pl, int B, int Hq, int Hkv, int MBPS,
-                     int NB, int P, int NP, hipStream_t s) {
+hipError_t launch_gc(int gc, const DecodeArgs& a, hipStream_t s) {
   switch (gc) {
-    case 1: return launch_t<BF16, D, BS, 1>(q, kc, vc, bt, cl, scale, out, po, pm, pl, B, Hq, Hkv, MBPS, NB, P, NP, s);
-    case 2: return launch_t<BF16, D, BS, 2>(q, kc, vc, bt, cl, scale, out, po, pm, pl, B, Hq, Hkv, MBPS, NB, P, NP, s);
-    case 4: return launch_t<BF16, D, BS, 4>(q, kc, vc, bt, cl, scale, out, po, pm, pl, B, Hq, Hkv, MBPS, NB, P, NP, s);
-    case 8: return launch_t<BF16, D, BS, 8>(q, kc, vc, bt, cl, scale, out, po, pm, pl, B, Hq, Hkv, MBPS, NB, P, NP, s);
+    case 1: return launch_t<BF16, D, BS, 1>(a, s);
+    case 2: return launch_t<BF16, D, BS, 2>(a, s);
+    case 4: return launch_t<BF16, D, BS, 4>(a, s);
+    case 8: return launch_t<BF16, D, BS, 8>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <bool BF16, int D>
-hipError_t launch_bs(int bs, int gc, const void* q, const void* kc, const void* vc, const int32_t* bt,
-                     const int32_t* cl, float scale, void* out, float* po, float* pm, float* pl, int B, int Hq,
-                     int Hkv, int MBPS, int NB, int P, int NP, hipStream_t s) {
-  switch (bs) {
-    case 8: return launch_gc<BF16, D, 8>(gc, q, kc, vc, bt, cl, scale, out, po, pm, pl, B, Hq, Hkv, MBPS, NB, P, NP, s);
-    case 16: return launch_gc<BF16, D, 16>(gc, q, kc, vc, bt, cl, scale, out, po, pm, pl, B, Hq, Hkv, MBPS, NB, P, NP, s);
-    case 32: return launch_gc<BF16, D, 32>(gc, q, kc, vc, bt, cl, scale, out, po, pm, pl, B, Hq, Hkv, MBPS, NB, P, NP, s);
+hipError_t launch_bs(int gc, const DecodeArgs& a, hipStream_t s) {
+  switch (a.block_size) {
+    case 8: return launch_gc<BF16, D, 8>(gc, a, s);
+    case 16: return launch_gc<BF16, D, 16>(gc, a, s);
+    case 32: return launch_gc<BF16, D, 32>(gc, a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -319,27 +323,57 @@ int heads_per_chunk(int group) {
   return 1;
 }
 
-hipError_t launch_paged_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                               const int32_t* context_lens, float scale, void* out, float* part_o, float* part_m,
-                               float* part_l, int batch, int num_q_heads, int num_kv_heads, int head_dim,
-                               int block_size, int max_blocks_per_seq, int num_blocks, int partition_size,
-                               int max_partitions, bool bf16, hipStream_t stream) {
-  if (mfma_decode_supported(bf16, head_dim, block_size))
-    return launch_paged_decode_mfma(q, k_cache, v_cache, block_tables, context_lens, scale, out, part_o, part_m,
-                                    part_l, batch, num_q_heads, num_kv_heads, head_dim, block_size,
-                                    max_blocks_per_seq, num_blocks, partition_size, max_partitions, stream);
-  const int gc = heads_per_chunk(num_q_heads / num_kv_heads);
-#define XS_ARGS                                                                                                 \
-  block_size, gc, q, k_cache, v_cache, block_tables, context_lens, scale, out, part_o, part_m, part_l, batch, \
-      num_q_heads, num_kv_heads, max_blocks_per_seq, num_blocks, partition_size, max_partitions, stream
-  if (bf16) {
-    if (head_dim == 64) return launch_bs<true, 64>(XS_ARGS);
-    if (head_dim == 128) return launch_bs<true, 128>(XS_ARGS);
-  } else {
-    if (head_dim == 64) return launch_bs<false, 64>(XS_ARGS);
-    if (head_dim == 128) return launch_bs<false, 128>(XS_ARGS);
+int device_cu_count() {
+  static std::atomic<int> cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int known = cache[dev].load(std::memory_order_relaxed);
+    if (known > 0) return known;
   }
-#undef XS_ARGS
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+DecodeParams make_params(const DecodeArgs& a, int heads_per_wave) {
+  DecodeParams p;
+  p.q = static_cast<const uint4*>(a.q);
+  p.k_cache = static_cast<const uint4*>(a.k_cache);
+  p.v_cache = static_cast<const uint4*>(a.v_cache);
+  p.block_tables = a.block_tables;
+  p.context_lens = a.context_lens;
+  p.k_new = static_cast<const uint4*>(a.k_new);
+  p.v_new = static_cast<const uint4*>(a.v_new);
+  p.k_cache_w = static_cast<uint4*>(a.k_cache);
+  p.v_cache_w = static_cast<uint4*>(a.v_cache);
+  p.scale_log2e = a.scale * kLog2e;
+  p.out = a.out;
+  p.part_o = a.part_o;
+  p.part_m = a.part_m;
+  p.part_l = a.part_l;
+  p.num_q_heads = a.num_q_heads;
+  p.num_kv_heads = a.num_kv_heads;
+  p.group = a.num_q_heads / a.num_kv_heads;
+  p.chunks = p.group / heads_per_wave;
+  p.max_blocks_per_seq = a.max_blocks_per_seq;
+  p.num_blocks = a.num_blocks;
+  p.part_blocks = a.partition_size > 0 ? a.partition_size / a.block_size : 0;
+  p.max_partitions = a.max_partitions;
+  return p;
+}
+
+hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
+  if (mfma_decode_supported(a.bf16, a.head_dim, a.block_size)) return launch_paged_decode_mfma(a, stream);
+  const int gc = heads_per_chunk(a.num_q_heads / a.num_kv_heads);
+  if (a.bf16) {
+    if (a.head_dim == 64) return launch_bs<true, 64>(gc, a, stream);
+    if (a.head_dim == 128) return launch_bs<true, 128>(gc, a, stream);
+  } else {
+    if (a.head_dim == 64) return launch_bs<false, 64>(gc, a, stream);
+    if (a.head_dim == 128) return launch_bs<false, 128>(gc, a, stream);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -5,23 +5,29 @@
 // phase8...phase13): for the GC query heads of one kv head, over a block range,
 //   s_t = scale * q_h . K_t,  m = max s_t,  l = sum exp(s_t - m),  o = sum exp(s_t - m) V_t / l.
 //
-// A work item (sequence, kv head, head chunk, partition) goes to one workgroup of four
-// wavefronts. The wavefronts take the item's 16-token tiles round-robin, each keeps its own
-// online-softmax state, and they merge through LDS at the end (max, rescale, add). Per tile:
+// A work item (sequence, kv head, head chunk, partition) goes to one workgroup of NW = 1, 2 or 4
+// wavefronts, chosen at launch so that the grid fills the GPU. The wavefronts take the item's
+// 16-token tiles round-robin, each keeps its own online-softmax state, and they merge through
+// LDS at the end (max, rescale, add). Per tile:
 //   QK  C[16 tokens x 16] = K_tile[16 x D] . Q^T[D x 16] with v_mfma_f32_16x16x32_bf16 (D/32 of
 //       them). The 16 columns hold the GC heads repeated, so lane l ends with the scores of
 //       tokens 4(l/16)+i (i = 0..3) for head (l%16) % GC. The A operand (K) needs lane l to hold
 //       16 bytes of token l%16, so each K load moves four 64-byte runs per token row.
 //   softmax  The running max is kept per head and shared by the whole wavefront: a tile max
 //       over the lane's 4 scores, then across the four lane rows. p = 2^(s*log2e*scale - m).
-//   PV  O[16 x D] += P[16 x 16 tokens] . V_tile[16 x D] with v_mfma_f32_16x16x16_bf16 (D/16 of
-//       them). The A operand (P, rounded to bf16) is exactly what the QK output left in each
-//       lane. The B operand needs 4 tokens of one d per lane: V goes through the wavefront's own
-//       LDS slice (rows padded to 2D+8 bytes so the four lane rows hit different banks) and comes
-//       back 2 bytes at a time.
+//   PV  O[4 heads x D] += P[4 heads x 4 tokens] . V[4 tokens x D] per group of 4 tokens, with
+//       v_mfma_f32_4x4x4_16b_bf16: its 16 blocks each take 4 columns of d, and all of them use
+//       the P operand of one block (CBSZ/ABID broadcast). That operand (P, rounded to bf16) is
+//       exactly what the QK output left in lanes 16kg..16kg+3. The B operand needs 4 tokens of
+//       one d per lane, so V goes through the wavefront's own LDS slice and comes back 2 bytes
+//       at a time; lane l reads column d = 64h + l, 128 consecutive bytes per wavefront.
+//       The accumulator is O[head][64h + lane]: D/16 registers, and the stores coalesce.
 // Tokens at or past L get score -inf and a zeroed V, so pool tails (NaN included) never reach
-// the result. Each wavefront loads its next tile into a second register set while it processes
-// the current one.
+// the result. K/V are read with nontemporal loads (each byte is used once). Each wavefront
+// loads its next tile into a second register set while it processes the current one.
+// Fused append (k_new non-null): every wavefront that loads the tile holding token L-1 takes
+// that token's K/V from k_new/v_new, and one wavefront writes them into the pools; no
+// wavefront reads the slot being written.
 #include <math.h>
 
 #include <type_traits>
@@ -69,12 +75,7 @@ __device__ __forceinline__ void wave_lds_fence() {
 
 template <int D, int BS, int GC, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(XS_DECODE_MIN_WAVES_PER_EU)))
-void paged_decode_mfma_kernel(
-    const uint4* __restrict__ q, const uint4* __restrict__ k_cache, const uint4* __restrict__ v_cache,
-    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens, float scale_log2e,
-    void* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_m, float* __restrict__ part_l,
-    int num_q_heads, int num_kv_heads, int group, int chunks, int max_blocks_per_seq, int num_blocks,
-    int part_blocks, int max_partitions) {
+void paged_decode_mfma_kernel(const DecodeParams prm) {
   constexpr int KK = D / 32;                // QK matrix ops per tile
   constexpr int NH = D / 64;                // 64-wide d halves of the PV output
   constexpr int HP = (GC + 3) / 4;          // PV passes of 4 heads
@@ -99,7 +100,10 @@ void paged_decode_mfma_kernel(
   const int c = lane & 15;  // column: token of the K operand; head c % GC of the scores
   unsigned char* vlds = smem + wave * STAGE_BYTES;
 
-  const bool split = part_blocks > 0;
+  const int num_kv_heads = prm.num_kv_heads;
+  const int max_blocks_per_seq = prm.max_blocks_per_seq;
+  const int max_partitions = prm.max_partitions;
+  const bool split = prm.part_blocks > 0;
   const int np = split ? max_partitions : 1;
   // Work items are numbered partition-major. The hardware deals workgroups round-robin to the
   // eight XCDs, so neighbouring ids must carry similar work: every (sequence, kv head) has a
@@ -109,32 +113,49 @@ void paged_decode_mfma_kernel(
   const unsigned per_p = gridDim.x / (unsigned)np;  // batch * num_kv_heads * chunks
   const int p = wg / per_p;
   wg %= per_p;
-  const int ch = wg % chunks;
-  wg /= chunks;
+  const int ch = wg % prm.chunks;
+  wg /= prm.chunks;
   const int g = wg % num_kv_heads;
   const int b = wg / num_kv_heads;
-  const int h0 = g * group + ch * GC;
+  const int h0 = g * prm.group + ch * GC;
 
-  int L = context_lens[b];
-  L = min(L, max_blocks_per_seq * BS);
+  const int L_in = prm.context_lens[b];
+  const int L = min(L_in, max_blocks_per_seq * BS);
   const int nblk_seq = L > 0 ? (L + BS - 1) / BS : 0;
   int jb = 0, je = nblk_seq;
   if (split) {
-    jb = p * part_blocks;
-    je = min(jb + part_blocks, nblk_seq);
+    jb = p * prm.part_blocks;
+    je = min(jb + prm.part_blocks, nblk_seq);
     if (jb >= je) return;  // the whole workgroup leaves together
   }
-  const size_t q_row0 = (size_t)b * num_q_heads + h0;
+  const size_t q_row0 = (size_t)b * prm.num_q_heads + h0;
   if (jb >= je) {  // no split, empty context
     if (wave == 0 && lane < GC * ROW16)
-      reinterpret_cast<uint4*>(out)[q_row0 * ROW16 + lane] = make_uint4(0, 0, 0, 0);
+      reinterpret_cast<uint4*>(prm.out)[q_row0 * ROW16 + lane] = make_uint4(0, 0, 0, 0);
     return;
+  }
+  const int32_t* bt = prm.block_tables + (size_t)b * max_blocks_per_seq;
+  auto valid = [&](int blk) { return blk >= 0 && blk < prm.num_blocks; };
+
+  // Fused append: token L-1 comes from k_new/v_new; the item holding it writes them to the pools.
+  const bool append = prm.k_new != nullptr && L_in >= 1 && L_in == L;
+  const int last = append ? L - 1 : -1;
+  const size_t new_row = ((size_t)b * num_kv_heads + g) * ROW16;
+  if (append && ch == 0 && wave == 0 && last / BS >= jb && last / BS < je && lane < 2 * ROW16) {
+    const int blk = bt[last / BS];
+    if (valid(blk)) {
+      const size_t dst = (((size_t)blk * num_kv_heads + g) * BS + last % BS) * ROW16;
+      if (lane < ROW16)
+        prm.k_cache_w[dst + lane] = prm.k_new[new_row + lane];
+      else
+        prm.v_cache_w[dst + lane - ROW16] = prm.v_new[new_row + lane - ROW16];
+    }
   }
 
   // B operand of QK: lane l holds q[h0 + c%GC][32kk + 8j .. +8].
   uint4 qop[KK];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) qop[kk] = q[(q_row0 + c % GC) * ROW16 + 4 * kk + j];
+  for (int kk = 0; kk < KK; ++kk) qop[kk] = prm.q[(q_row0 + c % GC) * ROW16 + 4 * kk + j];
 
   // acc[hp*NH + hf][i] = O[head 4hp+i][64hf + lane] (rows past GC repeat lower heads).
   float4_t acc[ACC];
@@ -142,8 +163,6 @@ void paged_decode_mfma_kernel(
   for (int a = 0; a < ACC; ++a) acc[a] = float4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf;  // running max of head c%GC (same in every lane of that head)
   float l_part = 0.f;     // this lane's share of the softmax sum of head c%GC
-
-  const int32_t* bt = block_tables + (size_t)b * max_blocks_per_seq;
 
   // Block ids of 64 consecutive blocks of the range sit in one VGPR, one per lane.
   int id_chunk = -1, ids = -1;
@@ -157,15 +176,21 @@ void paged_decode_mfma_kernel(
     }
     return __builtin_amdgcn_readlane(ids, rel & 63);
   };
-  auto valid = [&](int blk) { return blk >= 0 && blk < num_blocks; };
 
   // Tile loads. K: token c of the tile, pieces 4kk + j. V: pieces r*64 + lane of the tile.
-  auto load_tile = [&](int blk, int sub, uint4 (&kr)[KK], uint4 (&vr)[VL]) {
-    const size_t row0 = ((size_t)blk * num_kv_heads + g) * BS + sub * 16;
+  auto load_tile = [&](int blk, int tile, uint4 (&kr)[KK], uint4 (&vr)[VL]) {
+    const size_t row0 = ((size_t)blk * num_kv_heads + g) * BS + (tile % TPB) * 16;
+    const int tok0 = 16 * tile;
+    const uint4* ks = tok0 + c == last ? prm.k_new + new_row : prm.k_cache + (row0 + c) * ROW16;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) kr[kk] = k_cache[(row0 + c) * ROW16 + 4 * kk + j];
+    for (int kk = 0; kk < KK; ++kk) kr[kk] = load_stream(ks + 4 * kk + j);
 #pragma unroll
-    for (int r = 0; r < VL; ++r) vr[r] = v_cache[row0 * ROW16 + r * 64 + lane];
+    for (int r = 0; r < VL; ++r) {
+      const int piece = r * 64 + lane;
+      const uint4* vs = tok0 + piece / ROW16 == last ? prm.v_new + new_row + piece % ROW16
+                                                     : prm.v_cache + row0 * ROW16 + piece;
+      vr[r] = load_stream(vs);
+    }
   };
 
   auto process = [&](const uint4 (&kr)[KK], const uint4 (&vr)[VL], int nvalid) {
@@ -185,7 +210,7 @@ void paged_decode_mfma_kernel(
     float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sc[i] = s[i] * scale_log2e;
+      sc[i] = s[i] * prm.scale_log2e;
       if (4 * j + i >= nvalid) sc[i] = kNegInf;
     }
     float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
@@ -246,20 +271,20 @@ void paged_decode_mfma_kernel(
   int bA = -1, bB = -1;
   if (t < t_end) {
     bA = block_of(t);
-    if (valid(bA)) load_tile(bA, t % TPB, kA, vA);
+    if (valid(bA)) load_tile(bA, t, kA, vA);
   }
   while (t < t_end) {
     const int t2 = t + NW;
     if (t2 < t_end) {
       bB = block_of(t2);
-      if (valid(bB)) load_tile(bB, t2 % TPB, kB, vB);
+      if (valid(bB)) load_tile(bB, t2, kB, vB);
     }
     if (valid(bA)) process(kA, vA, min(16, L - 16 * t));
     if (t2 >= t_end) break;
     const int t3 = t2 + NW;
     if (t3 < t_end) {
       bA = block_of(t3);
-      if (valid(bA)) load_tile(bA, t3 % TPB, kA, vA);
+      if (valid(bA)) load_tile(bA, t3, kA, vA);
     }
     if (valid(bB)) process(kB, vB, min(16, L - 16 * t2));
     t = t3;
@@ -327,54 +352,47 @@ void paged_decode_mfma_kernel(
     const float inv = l_h[r] > 0.f ? 1.f / l_h[r] : 0.f;
     if (split) {
       const size_t prow = (q_row0 + r) * (size_t)max_partitions + p;
-      float* po = part_o + prow * D;
+      float* po = prm.part_o + prow * D;
 #pragma unroll
       for (int hf = 0; hf < NH; ++hf) po[64 * hf + lane] = acc[hp * NH + hf][i] * inv;
       if (lane == 0) {
-        part_m[prow] = m_h[r] == kNegInf ? kNegInf : m_h[r] * kLn2;
-        part_l[prow] = l_h[r];
+        prm.part_m[prow] = m_h[r] == kNegInf ? kNegInf : m_h[r] * kLn2;
+        prm.part_l[prow] = l_h[r];
       }
     } else {
-      uint16_t* o = reinterpret_cast<uint16_t*>(out) + (q_row0 + r) * D;
+      uint16_t* o = reinterpret_cast<uint16_t*>(prm.out) + (q_row0 + r) * D;
 #pragma unroll
       for (int hf = 0; hf < NH; ++hf) o[64 * hf + lane] = (uint16_t)f32_to_bf16_rne(acc[hp * NH + hf][i] * inv);
     }
   }
 }
 
-#ifndef XS_DECODE_WAVES_PER_UNIT
-#define XS_DECODE_WAVES_PER_UNIT 1
-#endif
-constexpr int kWavesPerUnit = XS_DECODE_WAVES_PER_UNIT;
-
 template <int D, int BS, int GC>
-hipError_t launch_t(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                    const int32_t* context_lens, float scale, void* out, float* part_o, float* part_m,
-                    float* part_l, int batch, int num_q_heads, int num_kv_heads, int max_blocks_per_seq,
-                    int num_blocks, int partition_size, int max_partitions, hipStream_t stream) {
-  const int group = num_q_heads / num_kv_heads;
-  const int chunks = group / GC;
-  const int part_blocks = partition_size > 0 ? partition_size / BS : 0;
-  const long long np = part_blocks > 0 ? max_partitions : 1;
-  const long long grid = (long long)batch * num_kv_heads * chunks * np;
-  hipLaunchKernelGGL((paged_decode_mfma_kernel<D, BS, GC, kWavesPerUnit>), dim3((unsigned)grid),
-                     dim3(64 * kWavesPerUnit), 0, stream,
-                     static_cast<const uint4*>(q), static_cast<const uint4*>(k_cache),
-                     static_cast<const uint4*>(v_cache), block_tables, context_lens, scale * kLog2e, out, part_o,
-                     part_m, part_l, num_q_heads, num_kv_heads, group, chunks, max_blocks_per_seq, num_blocks,
-                     part_blocks, max_partitions);
+hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+  const DecodeParams prm = make_params(a, GC);
+  const long long np = prm.part_blocks > 0 ? a.max_partitions : 1;
+  const long long grid = (long long)a.batch * a.num_kv_heads * prm.chunks * np;
+  // Wavefronts per work item: the most that keep the whole grid resident at once (4 per SIMD),
+  // or 4 when the grid needs several rounds anyway (finer pieces even out the last round).
+  const long long resident = 16LL * device_cu_count();
+  int nw = 4;
+  if (grid <= resident) nw = grid * 4 <= resident ? 4 : grid * 2 <= resident ? 2 : 1;
+  const dim3 g3((unsigned)grid);
+  switch (nw) {
+    case 1: hipLaunchKernelGGL((paged_decode_mfma_kernel<D, BS, GC, 1>), g3, dim3(64), 0, stream, prm); break;
+    case 2: hipLaunchKernelGGL((paged_decode_mfma_kernel<D, BS, GC, 2>), g3, dim3(128), 0, stream, prm); break;
+    default: hipLaunchKernelGGL((paged_decode_mfma_kernel<D, BS, GC, 4>), g3, dim3(256), 0, stream, prm); break;
+  }
   return hipGetLastError();
 }
 
 template <int D, int BS>
-hipError_t launch_gc(int gc, const void* q, const void* kc, const void* vc, const int32_t* bt, const int32_t* cl,
-                     float scale, void* out, float* po, float* pm, float* pl, int B, int Hq, int Hkv, int MBPS, int NB,
-                     int P, int NP, hipStream_t s) {
+hipError_t launch_gc(int gc, const DecodeArgs& a, hipStream_t s) {
   switch (gc) {
-    case 1: return launch_t<D, BS, 1>(q, kc, vc, bt, cl, scale, out, po, pm, pl, B, Hq, Hkv, MBPS, NB, P, NP, s);
-    case 2: return launch_t<D, BS, 2>(q, kc, vc, bt, cl, scale, out, po, pm, pl, B, Hq, Hkv, MBPS, NB, P, NP, s);
-    case 4: return launch_t<D, BS, 4>(q, kc, vc, bt, cl, scale, out, po, pm, pl, B, Hq, Hkv, MBPS, NB, P, NP, s);
-    case 8: return launch_t<D, BS, 8>(q, kc, vc, bt, cl, scale, out, po, pm, pl, B, Hq, Hkv, MBPS, NB, P, NP, s);
+    case 1: return launch_t<D, BS, 1>(a, s);
+    case 2: return launch_t<D, BS, 2>(a, s);
+    case 4: return launch_t<D, BS, 4>(a, s);
+    case 8: return launch_t<D, BS, 8>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -385,20 +403,12 @@ bool mfma_decode_supported(bool bf16, int head_dim, int block_size) {
   return bf16 && (head_dim == 64 || head_dim == 128) && (block_size == 16 || block_size == 32);
 }
 
-hipError_t launch_paged_decode_mfma(const void* q, const void* k_cache, const void* v_cache,
-                                    const int32_t* block_tables, const int32_t* context_lens, float scale, void* out,
-                                    float* part_o, float* part_m, float* part_l, int batch, int num_q_heads,
-                                    int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
-                                    int num_blocks, int partition_size, int max_partitions, hipStream_t stream) {
-  const int gc = heads_per_chunk(num_q_heads / num_kv_heads);
-#define XS_ARGS                                                                                                    \
-  gc, q, k_cache, v_cache, block_tables, context_lens, scale, out, part_o, part_m, part_l, batch, num_q_heads, \
-      num_kv_heads, max_blocks_per_seq, num_blocks, partition_size, max_partitions, stream
-  if (head_dim == 128 && block_size == 16) return launch_gc<128, 16>(XS_ARGS);
-  if (head_dim == 128 && block_size == 32) return launch_gc<128, 32>(XS_ARGS);
-  if (head_dim == 64 && block_size == 16) return launch_gc<64, 16>(XS_ARGS);
-  if (head_dim == 64 && block_size == 32) return launch_gc<64, 32>(XS_ARGS);
-#undef XS_ARGS
+hipError_t launch_paged_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
+  const int gc = heads_per_chunk(a.num_q_heads / a.num_kv_heads);
+  if (a.head_dim == 128 && a.block_size == 16) return launch_gc<128, 16>(gc, a, stream);
+  if (a.head_dim == 128 && a.block_size == 32) return launch_gc<128, 32>(gc, a, stream);
+  if (a.head_dim == 64 && a.block_size == 16) return launch_gc<64, 16>(gc, a, stream);
+  if (a.head_dim == 64 && a.block_size == 32) return launch_gc<64, 32>(gc, a, stream);
   return hipErrorInvalidValue;
 }
 

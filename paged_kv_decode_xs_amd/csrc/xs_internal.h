@@ -7,33 +7,69 @@
 
 namespace xs {
 
+// One decode launch. k_new/v_new non-null asks for the fused append: the kernel then takes the
+// K/V of token L_b - 1 from k_new/v_new and writes them into the pools, exactly as
+// launch_kv_append followed by a plain decode would.
+struct DecodeArgs {
+  const void* q;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const void* k_new;
+  const void* v_new;
+  float scale;
+  void* out;
+  float* part_o;
+  float* part_m;
+  float* part_l;
+  int batch, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks;
+  int partition_size, max_partitions;
+  bool bf16;
+};
+
+// What one decode kernel receives (by value, in the kernel argument segment).
+struct DecodeParams {
+  const uint4* q;
+  const uint4* k_cache;
+  const uint4* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const uint4* k_new;  // non-null: fused append
+  const uint4* v_new;
+  uint4* k_cache_w;    // the pools again, for the fused append's writes
+  uint4* v_cache_w;
+  float scale_log2e;
+  void* out;
+  float* part_o;
+  float* part_m;
+  float* part_l;
+  int num_q_heads, num_kv_heads, group, chunks, max_blocks_per_seq, num_blocks, part_blocks, max_partitions;
+};
+
+DecodeParams make_params(const DecodeArgs& a, int heads_per_wave);
+
 hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                             const int32_t* block_tables, const int32_t* context_lens, int batch,
                             int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
                             int num_blocks, int elt_bytes, hipStream_t stream);
 
-// Returns hipErrorInvalidValue for a shape without a compiled kernel (checked beforehand by the caller).
-hipError_t launch_paged_decode(const void* q, const void* k_cache, const void* v_cache,
-                               const int32_t* block_tables, const int32_t* context_lens, float scale,
-                               void* out, float* part_o, float* part_m, float* part_l, int batch,
-                               int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                               int max_blocks_per_seq, int num_blocks, int partition_size,
-                               int max_partitions, bool bf16, hipStream_t stream);
+// Picks the matrix-core kernel when it supports the shape, else the generic one.
+hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
 
 hipError_t launch_paged_reduce(const float* part_o, const float* part_m, const float* part_l,
                                const int32_t* context_lens, void* out, int batch, int num_q_heads,
                                int head_dim, int partition_size, int max_partitions, bool bf16,
                                hipStream_t stream);
 
-// Matrix-core variant of launch_paged_decode, for the shapes mfma_decode_supported accepts.
+// Matrix-core variant, for the shapes mfma_decode_supported accepts.
 bool mfma_decode_supported(bool bf16, int head_dim, int block_size);
-hipError_t launch_paged_decode_mfma(const void* q, const void* k_cache, const void* v_cache,
-                                    const int32_t* block_tables, const int32_t* context_lens, float scale, void* out,
-                                    float* part_o, float* part_m, float* part_l, int batch, int num_q_heads,
-                                    int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
-                                    int num_blocks, int partition_size, int max_partitions, hipStream_t stream);
+hipError_t launch_paged_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 
 // Heads handled together by one wavefront: the largest of 8, 4, 2, 1 that divides the group size.
 int heads_per_chunk(int group);
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
 
 }  // namespace xs

@@ -21,19 +21,35 @@ __global__ __launch_bounds__(64) void paged_reduce_kernel(const float* __restric
                                                           void* __restrict__ out, int num_q_heads,
                                                           int partition_size, int max_partitions) {
   constexpr int DPL = D / 64;  // output elements per lane
+  constexpr int PRE = 8;       // partitions whose o is fetched before the count is known
   const int lane = threadIdx.x;
   const size_t row = blockIdx.x;  // (b, h)
   const int b = (int)(row / num_q_heads);
-  const int L = context_lens[b];
-  int n = L > 0 ? (L + partition_size - 1) / partition_size : 0;
-  n = min(n, max_partitions);
   const float* pm = part_m + row * max_partitions;
   const float* pl = part_l + row * max_partitions;
   const float* po = part_o + row * max_partitions * D + (size_t)lane * DPL;
 
-  // Lane j holds partition j (64 at a time): its max, then its weight l_j 2^((m_j - M) log2e).
-  float M = -INFINITY;
-  for (int j = lane; j < n; j += 64) M = fmaxf(M, pm[j]);
+  // Loads that do not depend on L go out together with it: (m, l) of the first 64 slots and o of
+  // the first PRE slots, all inside this row's max_partitions slots. Slots at or past the
+  // partition count n are ignored below.
+  const int L = context_lens[b];
+  float mj = lane < max_partitions ? pm[lane] : -INFINITY;
+  float lj = lane < max_partitions ? pl[lane] : 0.f;
+  float opre[PRE][DPL];
+#pragma unroll
+  for (int u = 0; u < PRE; ++u) {
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) opre[u][e] = u < max_partitions ? po[(size_t)u * D + e] : 0.f;
+  }
+  int n = L > 0 ? (L + partition_size - 1) / partition_size : 0;
+  n = min(n, max_partitions);
+  if (lane >= n) {
+    mj = -INFINITY;
+    lj = 0.f;
+  }
+
+  float M = mj;
+  for (int j = lane + 64; j < n; j += 64) M = fmaxf(M, pm[j]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
 
@@ -45,10 +61,22 @@ __global__ __launch_bounds__(64) void paged_reduce_kernel(const float* __restric
     const float M2 = M * kLog2e;
     for (int base = 0; base < n; base += 64) {
       const int jj = base + lane;
-      const float w = jj < n ? pl[jj] * fast_exp2(fmaf(pm[jj], kLog2e, -M2)) : 0.f;
+      float w = 0.f;
+      if (jj < n) w = base == 0 ? lj * fast_exp2(fmaf(mj, kLog2e, -M2)) : pl[jj] * fast_exp2(fmaf(pm[jj], kLog2e, -M2));
       W += w;
       const int cnt = min(64, n - base);
       int k = 0;
+      if (base == 0) {
+#pragma unroll
+        for (int u = 0; u < PRE; ++u) {
+          if (u < cnt) {
+            const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) acc[e] = fmaf(wk, opre[u][e], acc[e]);
+          }
+        }
+        k = PRE;
+      }
       // Eight partitions per round so that their loads are in flight together.
       for (; k + 8 <= cnt; k += 8) {
         float o[8][DPL];

@@ -1,8 +1,9 @@
 """One decode step: KV append, split-K decode attention, log-sum-exp reduce.
 
 `DecodeStep` owns the step's output and partial buffers (allocated once, through torch) and
-chains the three library calls on one stream. With partition_size == 0 it issues the unsplit
-decode and no reduce.
+chains the library calls on one stream. With partition_size == 0 it issues the unsplit decode
+and no reduce. With fused=True the append and the decode are one call
+(xs_paged_attn_decode_append); otherwise they are xs_kv_append then xs_paged_attn_decode.
 """
 
 from __future__ import annotations
@@ -17,12 +18,13 @@ from . import _binding as xb
 class DecodeStep:
     def __init__(self, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
                  context_lens: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, scale: float,
-                 partition_size: int = 0, max_context_len: Optional[int] = None):
+                 partition_size: int = 0, max_context_len: Optional[int] = None, fused: bool = False):
         self.q, self.k_cache, self.v_cache = q, k_cache, v_cache
         self.block_tables, self.context_lens = block_tables, context_lens
         self.k_new, self.v_new = k_new, v_new
         self.scale = float(scale)
         self.partition_size = int(partition_size)
+        self.fused = bool(fused)
         B, Hq, D = q.shape
         self.out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
         if self.partition_size > 0:
@@ -51,8 +53,18 @@ class DecodeStep:
             xb.xs_paged_attn_reduce(self.part_o, self.part_m, self.part_l, self.context_lens, self.out,
                                     self.partition_size, stream=stream)
 
+    def append_and_attend(self, stream=None) -> None:
+        xb.xs_paged_attn_decode_append(self.q, self.k_new, self.v_new, self.k_cache, self.v_cache,
+                                       self.block_tables, self.context_lens, self.scale,
+                                       out=None if self.partition_size > 0 else self.out,
+                                       part_o=self.part_o, part_m=self.part_m, part_l=self.part_l,
+                                       partition_size=self.partition_size, stream=stream)
+
     def run(self, stream=None) -> torch.Tensor:
-        self.append(stream)
-        self.attend(stream)
+        if self.fused:
+            self.append_and_attend(stream)
+        else:
+            self.append(stream)
+            self.attend(stream)
         self.reduce(stream)
         return self.out

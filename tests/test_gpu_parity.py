@@ -38,7 +38,8 @@ def test_workload_full_size(name):
     ref = OracleResult(case, w.partition_size)
     err0, _, _ = check_case(case, 0, ref, label=f"{name} unsplit")
     err1, _, _ = check_case(case, w.partition_size, ref, check_pools=False, label=f"{name} split")
-    log(f"[gpu] {name}: max |err| unsplit {err0:.3g}, split {err1:.3g}")
+    err2, _, _ = check_case(case, w.partition_size, ref, label=f"{name} split fused", fused=True)
+    log(f"[gpu] {name}: max |err| unsplit {err0:.3g}, split {err1:.3g}, split+fused append {err2:.3g}")
 
 
 # ---------------------------------------------------------------- reduced shapes and edge cases
@@ -76,6 +77,7 @@ def test_shapes(idx):
     case = _shape_case(dtype, Hq, Hkv, D, BS, lens, seed=100 + idx)
     ref = OracleResult(case, P)
     check_case(case, 0, ref, label=f"shape{idx} unsplit")
+    check_case(case, 0, ref, label=f"shape{idx} unsplit fused", fused=True)
     check_case(case, P, ref, check_pools=False, label=f"shape{idx} split")
     # Partition = one block: many partitions per sequence.
     check_case(case, BS, OracleResult(case, BS), check_pools=False, label=f"shape{idx} P=BS")
@@ -140,3 +142,24 @@ def test_stream_argument_is_honoured():
     from tests.gpu_common import TOL, assert_close
 
     assert_close(as_f64(step.out), ref.out, *TOL["bf16"], "side stream")
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,BS,lens,P", [
+    ("bf16", 32, 8, 128, 16, [1, 16, 17, 2000, 0], 64),   # matrix-core kernel
+    ("bf16", 16, 2, 64, 32, [33, 31, 100], 32),           # matrix-core kernel, group 8, two tiles per block
+    ("bf16", 12, 12, 64, 8, [9, 200], 16),                # generic kernel (block_size 8)
+    ("f32", 8, 2, 128, 16, [5, 77], 32),                  # generic kernel (fp32)
+])
+def test_fused_append_is_bitwise_the_two_calls(dtype, Hq, Hkv, D, BS, lens, P):
+    case = _shape_case(dtype, Hq, Hkv, D, BS, lens, seed=31)
+    maxlen = max(lens)
+    for part in (0, P):
+        a = case_to_device(case)
+        s1 = run_step(a, case.workload.scale, part, maxlen, fused=False)
+        b = case_to_device(case)
+        s2 = run_step(b, case.workload.scale, part, maxlen, fused=True)
+        view = torch.int16 if dtype == "bf16" else torch.int32
+        assert torch.equal(s1.out.view(view), s2.out.view(view)), f"outputs differ (P={part})"
+        for name in ("k_cache", "v_cache"):
+            assert torch.equal(a[name].view(view), b[name].view(view)), f"{name} differs (P={part})"
+    log(f"[gpu] fused append: bitwise equal to append + decode for {dtype} D={D} BS={BS}")
