@@ -9,8 +9,10 @@ Prints ONE JSON line on stdout (diagnostics go to stderr):
   roofline      the decode kernel alone: its algorithmic bytes per launch / its mean duration
                 (HIP events around each decode launch, on the launch stream, in a second pass
                 of the same K steps) vs 8 TB/s;
-                `traffic` comes from the rocprofv3 FETCH_SIZE/WRITE_SIZE summary committed
-                in profiles/, and is null when the kernel source changed since it was taken
+                `traffic` is the HBM bytes per launch counted by rocprofv3 (FETCH_SIZE and
+                WRITE_SIZE, calibrated on a 1 GiB copy; the summary is committed in profiles/)
+                over the same mean duration, in GB/s like `achieved`; null when the kernel
+                source changed since the counters were taken
   cpu_baseline  the fp64 oracle timed on the host over a bounded sample of the same workload;
                 its output is also compared with the GPU's for those sequences
 
@@ -147,6 +149,9 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=None, help="pool copies to rotate through")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed work, copy a 1 GiB buffer 5 times with torch (a plain copy kernel of "
+                         "known size, to calibrate rocprofv3's FETCH_SIZE/WRITE_SIZE)")
     ap.add_argument("--no-fuse", action="store_true",
                     help="issue xs_kv_append and xs_paged_attn_decode separately instead of the fused call")
     args = ap.parse_args()
@@ -226,11 +231,38 @@ def main() -> int:
     decode_ms = [a.elapsed_time(b) for a, b in ev]
     decode_ms_mean = float(np.mean(decode_ms))
 
+    # Reference read rate of the device: the library's streaming-read probe over 2 GiB.
+    probe_buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    probe_buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    achievable = {}
+    for nt in (False, True):
+        xs.xs_stream_read_probe(probe_buf, sink, nontemporal=nt, stream=stream)
+        best = float("inf")
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            xs.xs_stream_read_probe(probe_buf, sink, nontemporal=nt, stream=stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(b))
+        achievable["nontemporal" if nt else "plain"] = round(probe_buf.numel() / (best * 1e-3) / 1e9, 1)
+    del probe_buf
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     ab = algorithmic_bytes(case, P)
     kv_gbs = ab["kv"] / (ms_step * 1e-3) / 1e9
     decode_bytes = ab["decode"] + (ab["append"] if fused else 0)
     achieved = decode_bytes / (decode_ms_mean * 1e-3) / 1e9
-    traffic = read_traffic(w.name, P, fused)
+    traffic_bytes = read_traffic(w.name, P, fused)
+    traffic = None if traffic_bytes is None else round(traffic_bytes / (decode_ms_mean * 1e-3) / 1e9, 2)
     result = {
         "metric": METRIC,
         "value": round(kv_gbs, 2),
@@ -260,6 +292,8 @@ def main() -> int:
         },
         "seqs_per_s": round(w.batch / (ms_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100 * kv_gbs / HBM_PEAK_GBS, 2),
+        "achievable_read_GBps": achievable,
+        "pct_of_achievable_nontemporal_read": round(100 * kv_gbs / achievable["nontemporal"], 2),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -269,6 +303,7 @@ def main() -> int:
             "traffic": traffic,
             "kernel": "paged_decode_mfma_kernel" + (" (fused append)" if fused else ""),
             "algorithmic_bytes_per_launch": decode_bytes,
+            "traffic_bytes_per_launch": traffic_bytes,
             "mean_launch_us": round(decode_ms_mean * 1e3, 2),
         },
     }

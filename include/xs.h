@@ -46,6 +46,7 @@
 #ifndef XS_H
 #define XS_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -144,6 +145,15 @@ int xs_paged_attn_reduce(const float* part_o, const float* part_m, const float* 
                          const int32_t* context_lens, void* out,
                          int batch, int num_q_heads, int head_dim,
                          int partition_size, int max_partitions, int dtype, void* stream);
+
+/*
+ * Measurement aid, not part of the decode step: reads `bytes` (a multiple of 16) at `buf` with
+ * 16-byte loads (nontemporal if `nontemporal` != 0) in a grid-stride loop, and writes at most
+ * one word to `sink` (device memory, 4 bytes). Timing it gives the read rate that plain
+ * streaming reaches on the device, the reference the decode kernel's bandwidth is compared
+ * with. `buf` must be 16-byte aligned.
+ */
+int xs_stream_read_probe(const void* buf, size_t bytes, unsigned* sink, int nontemporal, void* stream);
 
 /* Message for the last nonzero status returned on this thread ("" if none). Host memory owned
  * by the library, valid until the next call on this thread. */

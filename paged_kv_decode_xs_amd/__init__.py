@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     xs_paged_attn_decode,
     xs_paged_attn_decode_append,
     xs_paged_attn_reduce,
+    xs_stream_read_probe,
     xs_version,
 )
 from .step import DecodeStep  # noqa: F401

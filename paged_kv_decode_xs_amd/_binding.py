@@ -40,6 +40,7 @@ SIGNATURES = {
     "xs_paged_attn_decode_append": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _vp,
                                     _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp],
     "xs_paged_attn_reduce": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp],
+    "xs_stream_read_probe": [_vp, ctypes.c_size_t, _vp, _i, _vp],
     "xs_last_error": [],
     "xs_version": [],
 }
@@ -205,6 +206,15 @@ def xs_paged_attn_reduce(part_o: torch.Tensor, part_m: torch.Tensor, part_l: tor
     _check("xs_paged_attn_reduce", lib.xs_paged_attn_reduce(
         _ptr(part_o), _ptr(part_m), _ptr(part_l), _ptr(context_lens), _ptr(out), B, Hq, D,
         int(partition_size), NP, _dtype_code(out), _stream_handle(stream)))
+
+
+def xs_stream_read_probe(buf: torch.Tensor, sink: torch.Tensor, nontemporal: bool = True, stream=None) -> None:
+    """Read all of `buf` with 16-byte loads (a bandwidth reference); `sink` is a 4-byte device buffer."""
+    _dev(buf, sink)
+    nbytes = buf.numel() * buf.element_size()
+    _need(sink.numel() * sink.element_size() >= 4, "sink must hold 4 bytes")
+    _check("xs_stream_read_probe", load_library().xs_stream_read_probe(
+        _ptr(buf), nbytes - nbytes % 16, _ptr(sink), int(bool(nontemporal)), _stream_handle(stream)))
 
 
 def num_partitions(max_context_len: int, partition_size: int) -> int:

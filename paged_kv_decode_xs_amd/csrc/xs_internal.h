@@ -69,6 +69,9 @@ hipError_t launch_paged_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 // Heads handled together by one wavefront: the largest of 8, 4, 2, 1 that divides the group size.
 int heads_per_chunk(int group);
 
+// Streaming-read probe over `bytes` (a multiple of 16) of device memory.
+hipError_t launch_stream_read(const void* buf, size_t bytes, unsigned* sink, bool nontemporal, hipStream_t stream);
+
 // Compute units of the current device (cached per device).
 int device_cu_count();
 

@@ -133,3 +133,22 @@ def test_reduce_rejects(kw, status, needle):
 def test_binding_raises_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         xb.load_library(str(tmp_path / "nope.so"))
+
+
+def test_probe_rejects():
+    lib = xb.load_library()
+    assert lib.xs_stream_read_probe(None, 64, FAKE, 1, None) == 1
+    assert "NULL" in xb.xs_last_error()
+    assert lib.xs_stream_read_probe(FAKE, 24, FAKE, 1, None) == 1
+    assert "multiple of 16" in xb.xs_last_error()
+
+
+def test_decode_append_rejects_missing_new_rows():
+    lib = xb.load_library()
+    args = [FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 0.125, FAKE, None, None, None, 2, 8, 2, 128, 16, 4, 16, 0, 0, B,
+            None]
+    assert lib.xs_paged_attn_decode_append(*args) == 1
+    assert "k_new" in xb.xs_last_error()
+    args[0] = None  # q
+    assert lib.xs_paged_attn_decode_append(*args) == 1
+    assert "NULL" in xb.xs_last_error()
