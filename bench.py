@@ -40,7 +40,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 METRIC = "paged decode attention KV GB/s (% of HBM peak) + seqs/s, Qwen3-8B GQA shape"
 DECODE_SOURCES = ["paged_kv_decode_xs_amd/csrc/xs_decode.hip", "paged_kv_decode_xs_amd/csrc/xs_decode_mfma.hip",
-                  "paged_kv_decode_xs_amd/csrc/xs_device.h"]
+                  "paged_kv_decode_xs_amd/csrc/xs_mfma_tile.h", "paged_kv_decode_xs_amd/csrc/xs_device.h"]
 
 
 def log(msg: str) -> None:

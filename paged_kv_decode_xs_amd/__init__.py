@@ -14,7 +14,9 @@ from ._binding import (  # noqa: F401
     xs_kv_append,
     xs_last_error,
     xs_paged_attn_decode,
+    xs_paged_attn_balanced_workspace_size,
     xs_paged_attn_decode_append,
+    xs_paged_attn_decode_balanced,
     xs_paged_attn_reduce,
     xs_stream_read_probe,
     xs_version,

@@ -4,6 +4,8 @@
 chains the library calls on one stream. With partition_size == 0 it issues the unsplit decode
 and no reduce. With fused=True the append and the decode are one call
 (xs_paged_attn_decode_append); otherwise they are xs_kv_append then xs_paged_attn_decode.
+With schedule="balanced" the step is xs_paged_attn_decode_balanced (append included when fused;
+otherwise xs_kv_append first), which writes `out` itself; partition_size is then unused.
 """
 
 from __future__ import annotations
@@ -18,13 +20,17 @@ from . import _binding as xb
 class DecodeStep:
     def __init__(self, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
                  context_lens: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, scale: float,
-                 partition_size: int = 0, max_context_len: Optional[int] = None, fused: bool = False):
+                 partition_size: int = 0, max_context_len: Optional[int] = None, fused: bool = False,
+                 schedule: str = "split"):
         self.q, self.k_cache, self.v_cache = q, k_cache, v_cache
         self.block_tables, self.context_lens = block_tables, context_lens
         self.k_new, self.v_new = k_new, v_new
         self.scale = float(scale)
         self.partition_size = int(partition_size)
         self.fused = bool(fused)
+        if schedule not in ("split", "balanced"):
+            raise ValueError(f"unknown schedule {schedule!r}")
+        self.schedule = schedule
         B, Hq, D = q.shape
         self.out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
         if self.partition_size > 0:
@@ -37,6 +43,12 @@ class DecodeStep:
             self.part_l = torch.empty((B, Hq, NP), dtype=torch.float32, device=q.device)
         else:
             self.part_o = self.part_m = self.part_l = None
+        self.workspace = None
+        if schedule == "balanced":
+            self.partition_size = 0
+            self.part_o = self.part_m = self.part_l = None
+            nbytes = xb.xs_paged_attn_balanced_workspace_size(B, Hq, k_cache.shape[1], D)
+            self.workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
 
     def append(self, stream=None) -> None:
         xb.xs_kv_append(self.k_new, self.v_new, self.k_cache, self.v_cache, self.block_tables, self.context_lens,
@@ -60,7 +72,18 @@ class DecodeStep:
                                        part_o=self.part_o, part_m=self.part_m, part_l=self.part_l,
                                        partition_size=self.partition_size, stream=stream)
 
+    def balanced(self, stream=None) -> None:
+        xb.xs_paged_attn_decode_balanced(self.q, self.k_cache, self.v_cache, self.block_tables, self.context_lens,
+                                         self.scale, self.out, self.workspace,
+                                         k_new=self.k_new if self.fused else None,
+                                         v_new=self.v_new if self.fused else None, stream=stream)
+
     def run(self, stream=None) -> torch.Tensor:
+        if self.schedule == "balanced":
+            if not self.fused:
+                self.append(stream)
+            self.balanced(stream)
+            return self.out
         if self.fused:
             self.append_and_attend(stream)
         else:
