@@ -100,3 +100,18 @@ def test_balanced_fused_append_matches_separate_append():
     assert torch.equal(s1.out.view(torch.int16), s2.out.view(torch.int16))
     for name in ("k_cache", "v_cache"):
         assert torch.equal(a[name].view(torch.int16), b[name].view(torch.int16)), name
+
+
+def test_balanced_many_short_sequences():
+    # Workers cross hundreds of segment boundaries: pieces, slots and merges of short segments.
+    w = wl.WORKLOADS["qwen3_8b_b64"].with_(batch=2000, ctx=("uniform", 1, 48), max_blocks_per_seq=3)
+    case = wl.make_case(w, seed=31)
+    check_case(case, 0, OracleResult(case), label="balanced 2000 short", fused=True, schedule="balanced")
+
+
+@pytest.mark.slow
+def test_balanced_long_sequences():
+    # 32 x ~14k tokens: every worker's range lies inside one or two long segments.
+    w = wl.WORKLOADS["qwen3_8b_b64"].with_(batch=32, ctx=("uniform", 12000, 16000), max_blocks_per_seq=1000)
+    case = wl.make_case(w, seed=37)
+    check_case(case, 0, OracleResult(case), label="balanced long", fused=True, schedule="balanced")
