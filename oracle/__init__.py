@@ -14,7 +14,9 @@ Contents:
   softmax(q K^T * scale) V, per-partition softmax statistics with their
   log-sum-exp merge, and the naive causal attention it must agree with at the
   last position.
-* ``brute_force``: the same definition again, in Python ``decimal`` at
+* ``sinks_window``: the same decode with per-head attention sinks and a
+  sliding window, unsplit and split (the sink joins once, in the merge).
+* ``brute_force``: the definitions again, in Python ``decimal`` at
   40 digits over flat offsets, for tiny inputs only.
 
 Every function is pinned by the CPU tests in ``tests/test_oracle_*.py``
@@ -33,4 +35,11 @@ from .paged_attention import (  # noqa: F401
     lse_merge,
     split_paged_decode_attention,
     naive_causal_attention,
+)
+from .sinks_window import (  # noqa: F401
+    window_start,
+    paged_decode_attention_sinks,
+    partition_stats_window,
+    lse_merge_sink,
+    split_paged_decode_attention_sinks,
 )

@@ -64,3 +64,49 @@ def test_mutant_is_caught(name):
         except Exception as e:  # noqa: BLE001 - any failure of a pin counts as a catch
             failed.append((pin.__name__, type(e).__name__))
     assert failed, f"mutant {name} passed every pin"
+
+
+# Mistakes planted in the sinks / sliding-window oracle; each must fail one of SINK_PINS.
+import oracle.sinks_window as sw_mod  # noqa: E402
+from tests.oracle_pins_sinks import SINK_PINS  # noqa: E402
+
+SW_SOURCE = inspect.getsource(sw_mod)
+SW_MUTANTS = {
+    "sink_dropped": ("paged_decode_attention_sinks", "den = w.sum() + (0.0 if sig is None else np.exp(sig[h] - M))",
+                     "den = w.sum()"),
+    "sink_scaled": ("paged_decode_attention_sinks", "np.exp(sig[h] - M))", "np.exp(scale * sig[h] - M))"),
+    "sink_sign": ("paged_decode_attention_sinks", "np.exp(sig[h] - M))", "np.exp(-sig[h] - M))"),
+    "window_one_more": ("window_start", "max(0, L - window)", "max(0, L - window - 1)"),
+    "window_one_less": ("window_start", "max(0, L - window)", "max(0, L - window + 1)"),
+    "window_ignored": ("paged_decode_attention_sinks", "        t0 = window_start(L, window)\n", "        t0 = 0\n"),
+    "merge_sink_dropped": ("lse_merge_sink", "den = w.sum() + (0.0 if sink is None else np.exp(sink - M))",
+                           "den = w.sum()"),
+    "partition_start_unwindowed": ("partition_stats_window", "max(j * partition_size, t0)", "j * partition_size"),
+    "partition_first_index": ("partition_stats_window", "j0 = t0 // partition_size", "j0 = 0"),
+}
+
+
+def _mutate_sw(name):
+    func, old, new = SW_MUTANTS[name]
+    start = SW_SOURCE.index(f"\ndef {func}(")
+    end = SW_SOURCE.find("\ndef ", start + 1)
+    end = len(SW_SOURCE) if end < 0 else end
+    body = SW_SOURCE[start:end]
+    assert body.count(old) == 1, f"mutation text for {name} must occur exactly once in {func}"
+    src = SW_SOURCE[:start] + body.replace(old, new) + SW_SOURCE[end:]
+    src = src.replace("from .paged_attention import", "from oracle.paged_attention import")
+    mod = types.ModuleType(f"oracle_sw_mutant_{name}")
+    exec(compile(src, f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(SW_MUTANTS))
+def test_sinks_window_mutant_is_caught(name):
+    mod = _mutate_sw(name)
+    failed = []
+    for pin in SINK_PINS:
+        try:
+            pin(mod)
+        except Exception as e:  # noqa: BLE001 - any failure of a pin counts as a catch
+            failed.append((pin.__name__, type(e).__name__))
+    assert failed, f"mutant {name} passed every pin"
