@@ -76,22 +76,25 @@ def read_traffic(workload: str, partition: int, fused: bool):
 
 
 def algorithmic_bytes(case, partition: int):
-    """Bytes the step must move, by kernel (the method's own data, nothing padded)."""
+    """Bytes the step must move, by kernel (the method's own data, nothing padded). With a
+    sliding window only the positions in the window, their blocks and their partitions count."""
     w = case.workload
-    L = case.context_lens.astype(np.int64)
+    L = np.maximum(case.context_lens.astype(np.int64), 0)
+    t0 = np.maximum(L - w.window, 0) if w.window > 0 else np.zeros_like(L)
     B, Hq, Hkv, D, BS, e = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.elt_bytes
-    kv = int(L.sum()) * Hkv * D * e * 2
-    ids = 4 * int(((L + BS - 1) // BS).sum())
+    kv = case.kv_bytes()
+    ids = 4 * int(((L + BS - 1) // BS - t0 // BS).sum())
     q = B * Hq * D * e
     out = B * Hq * D * e
     lens = 4 * B
+    sinks = Hq * e if w.sinks else 0
     if partition > 0:
-        nparts = int(((L + partition - 1) // partition).sum())
+        nparts = int(((L + partition - 1) // partition - t0 // partition).sum())
         partials = nparts * Hq * (D + 2) * 4
         decode = kv + ids + q + lens + partials
-        reduce = partials + lens + out
+        reduce = partials + lens + out + sinks
     else:
-        decode = kv + ids + q + lens + out
+        decode = kv + ids + q + lens + out + sinks
         reduce = 0
     append = 4 * B * Hkv * D * e + 4 * B + lens  # read k_new/v_new, write their slots, one block id per sequence
     return {"kv": kv, "decode": decode, "reduce": reduce, "append": append, "step": decode + reduce + append}
@@ -139,61 +142,42 @@ def cpu_baseline(case, gpu_out, budget_s: float):
     }, {"sequences_checked": done, "max_abs_err": max_err, "out_of_tolerance": bad}
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="qwen3_8b_b64")
-    ap.add_argument("--partition", type=int, default=None, help="split-K partition size (0 = no split)")
-    ap.add_argument("--copies", type=int, default=None, help="pool copies to rotate through")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="after the timed work, copy a 1 GiB buffer 5 times with torch (a plain copy kernel of "
-                         "known size, to calibrate rocprofv3's FETCH_SIZE/WRITE_SIZE)")
-    ap.add_argument("--no-fuse", action="store_true",
-                    help="issue xs_kv_append and xs_paged_attn_decode separately instead of the fused call")
-    args = ap.parse_args()
+# Workloads measured after the headline one, each on its own line in "extra_workloads".
+EXTRA_WORKLOADS = ["gptoss_20b_window128_b64"]
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: every step runs on a single device "
-              "(run with --gpus 1)", file=sys.stderr)
-        return 2
 
+def run_workload(w, P: int, fused: bool, K: int, warmup: int, copies=None):
+    """Generate, upload and time one workload: K back-to-back steps (no events inside), then the
+    same K steps again with HIP events around each decode launch."""
     import torch
 
     import paged_kv_decode_xs_amd as xs
     import workloads as wl
     from workloads.device import case_to_device
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 1
-    torch.cuda.set_device(0)
-    xs.load_library()  # raises if libxs.so is missing: there is no fallback path
-
-    w = wl.WORKLOADS[args.workload]
-    P = w.partition_size if args.partition is None else args.partition
     t0 = time.time()
     case = wl.make_case(w)
     log(f"[bench] {w.name}: generated in {time.time() - t0:.1f}s, NB={case.num_blocks}, "
-        f"sum L={int(case.context_lens.sum())}, K+V={case.kv_bytes() / 1e9:.3f} GB")
+        f"sum L={int(case.context_lens.sum())}, K+V read per step={case.kv_bytes() / 1e9:.4f} GB")
     dev = case_to_device(case, "cuda:0")
+    sinks = None
+    if case.sinks is not None:
+        sinks = torch.from_numpy(case.sinks.view(np.int16).copy()).view(torch.bfloat16).to("cuda:0")
     pool_bytes = 2 * dev["k_cache"].numel() * dev["k_cache"].element_size()
-    R = args.copies or max(2, math.ceil(3e9 / pool_bytes))
+    # Enough copies that > 3 GB of pool, and > 768 MB of the bytes a step reads, pass between two
+    # uses of one copy: the 256 MB Infinity Cache then holds none of what a step reads.
+    R = copies or max(2, math.ceil(3e9 / pool_bytes), math.ceil(768e6 / max(case.kv_bytes(), 1)))
+    R = max(1, min(R, int(48e9 // pool_bytes)))
     pools = [(dev["k_cache"], dev["v_cache"])] + [(dev["k_cache"].clone(), dev["v_cache"].clone())
                                                    for _ in range(R - 1)]
     maxlen = int(case.context_lens.max())
-    fused = not args.no_fuse
     steps = [xs.DecodeStep(dev["q"], kc, vc, dev["block_tables"], dev["context_lens"], dev["k_new"], dev["v_new"],
-                           w.scale, partition_size=P, max_context_len=maxlen, fused=fused) for kc, vc in pools]
+                           w.scale, partition_size=P, max_context_len=maxlen, fused=fused, sinks=sinks,
+                           window=w.window) for kc, vc in pools]
     stream = torch.cuda.current_stream()
-    for i in range(args.warmup):
+    for i in range(warmup):
         steps[i % R].run(stream)
     torch.cuda.synchronize()
-
-    K = args.steps
 
     def one_step(i, ev=None):
         s = steps[i % R]
@@ -218,8 +202,7 @@ def main() -> int:
         one_step(i)
     end.record(stream)
     torch.cuda.synchronize()
-    ms_total = start.elapsed_time(end)
-    ms_step = ms_total / K
+    ms_step = start.elapsed_time(end) / K
 
     # The decode kernel alone: the same K steps again, with HIP events around each decode launch on
     # its stream (events between launches add a few microseconds of GPU time, so they stay out of
@@ -228,8 +211,76 @@ def main() -> int:
     for i in range(K):
         one_step(i, ev[i])
     torch.cuda.synchronize()
-    decode_ms = [a.elapsed_time(b) for a, b in ev]
-    decode_ms_mean = float(np.mean(decode_ms))
+    decode_ms_mean = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    out = steps[(K - 1) % R].out.float().cpu().double().numpy()
+    del steps, pools, dev
+    return {"case": case, "R": R, "ms_step": ms_step, "decode_ms_mean": decode_ms_mean, "out": out}
+
+
+def extra_row(w, P: int, fused: bool, r) -> dict:
+    """One line of "extra_workloads": the same quantities as the headline, for another workload."""
+    case = r["case"]
+    ab = algorithmic_bytes(case, P)
+    decode_bytes = ab["decode"] + (ab["append"] if fused else 0)
+    achieved = decode_bytes / (r["decode_ms_mean"] * 1e-3) / 1e9
+    return {
+        "workload": w.name,
+        "description": w.description,
+        "partition_size": P,
+        "window": w.window,
+        "sinks": w.sinks,
+        "pool_copies_rotated": r["R"],
+        "kv_bytes_per_step": ab["kv"],
+        "ms_per_step": round(r["ms_step"], 5),
+        "kv_GBps": round(ab["kv"] / (r["ms_step"] * 1e-3) / 1e9, 2),
+        "seqs_per_s": round(w.batch / (r["ms_step"] * 1e-3), 1),
+        "decode_launch_us": round(r["decode_ms_mean"] * 1e3, 2),
+        "decode_algorithmic_GBps": round(achieved, 2),
+        "decode_frac_of_hbm_peak": round(achieved / HBM_PEAK_GBS, 4),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen3_8b_b64")
+    ap.add_argument("--partition", type=int, default=None, help="split-K partition size (0 = no split)")
+    ap.add_argument("--copies", type=int, default=None, help="pool copies to rotate through")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the extra workloads")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed work, copy a 1 GiB buffer 5 times with torch (a plain copy kernel of "
+                         "known size, to calibrate rocprofv3's FETCH_SIZE/WRITE_SIZE)")
+    ap.add_argument("--no-fuse", action="store_true",
+                    help="issue xs_kv_append and xs_paged_attn_decode separately instead of the fused call")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: every step runs on a single device "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import paged_kv_decode_xs_amd as xs
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    xs.load_library()  # raises if libxs.so is missing: there is no fallback path
+
+    w = wl.WORKLOADS[args.workload]
+    P = w.partition_size if args.partition is None else args.partition
+    fused = not args.no_fuse
+    K = args.steps
+    r = run_workload(w, P, fused, K, args.warmup, args.copies)
+    case, R, ms_step, decode_ms_mean = r["case"], r["R"], r["ms_step"], r["decode_ms_mean"]
+    stream = torch.cuda.current_stream()
 
     # Reference read rate of the device: the library's streaming-read probe over 2 GiB.
     probe_buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
@@ -308,12 +359,21 @@ def main() -> int:
         },
     }
     if not args.no_cpu_baseline:
-        out = steps[(K - 1) % R].out.float().cpu().double().numpy()
-        cpu, parity = cpu_baseline(case, out, args.cpu_budget)
+        cpu, parity = cpu_baseline(case, r["out"], args.cpu_budget)
         result["cpu_baseline"] = cpu
         result["parity_vs_oracle"] = parity
         if parity["out_of_tolerance"]:
             log(f"[bench] PARITY FAILURE: {parity}")
+    if not args.no_extra:
+        rows = []
+        for name in EXTRA_WORKLOADS:
+            if name == w.name:
+                continue
+            we = wl.WORKLOADS[name]
+            torch.cuda.empty_cache()
+            rows.append(extra_row(we, we.partition_size, fused,
+                                  run_workload(we, we.partition_size, fused, min(K, 100), args.warmup)))
+        result["extra_workloads"] = rows
     print(json.dumps(result), flush=True)
     return 0 if result.get("parity_vs_oracle", {}).get("out_of_tolerance", 0) == 0 else 3
 

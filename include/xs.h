@@ -159,6 +159,47 @@ int xs_paged_attn_decode_balanced(const void* q, const void* k_new, const void* 
 size_t xs_paged_attn_balanced_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim);
 
 /*
+ * Decode attention with attention sinks and a sliding window (xserv compare
+ * phase10...cf1e9e41, attention.rs, `paged_decode_attention_sinks` and its FFI
+ * `launch_paged_decode_attention_sinks_bf16`), optionally with the fused append.
+ *
+ * sinks: NULL, or bf16 [num_q_heads] (device, read): one logit sigma_h per query head in the
+ *   units of the scaled scores. It joins the softmax as an entry without a value row.
+ * window_size: 0 keeps all positions; W > 0 keeps positions t in [max(0, L_b - W), L_b), the
+ *   query's own position L_b - 1 included.
+ * Result, for t0 = max(0, L_b - W) (or 0) and M = max(sigma_h, max_t s_t):
+ *   out[b, h, :] = sum_{t >= t0} exp(s_t - M) V_t / (exp(sigma_h - M) + sum_{t >= t0} exp(s_t - M)).
+ * L_b = 0 gives zeros. k_new/v_new: both NULL (no append) or both given, as in
+ * xs_paged_attn_decode_append. Other arguments, layouts and partitions as in
+ * xs_paged_attn_decode, except that with split-K partitions wholly before t0 are not written
+ * and the partials carry no sink: xs_paged_attn_reduce_sinks, with the same sinks and window,
+ * produces `out`.
+ * Supported: bf16, head_dim 64 or 128, block_size 16 or 32 (XS_EUNSUPPORTED otherwise).
+ * Readings where the pages are silent (sink units, window bounds, empty context) are the
+ * plainest ones the pages support; the oracle states them.
+ */
+int xs_paged_attn_decode_sinks(const void* q, const void* k_new, const void* v_new,
+                               void* k_cache, void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               const void* sinks, int window_size, float scale, void* out,
+                               float* part_o, float* part_m, float* part_l,
+                               int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                               int block_size, int max_blocks_per_seq, int num_blocks,
+                               int partition_size, int max_partitions, int dtype, void* stream);
+
+/*
+ * The merge of xs_paged_attn_decode_sinks' partials (same sinks and window_size): partitions
+ * j in [t0 / P, ceil(L_b / P)) with t0 the window start, and
+ *   M = max(sigma_h, max_j m_j),
+ *   out = sum_j l_j e^(m_j - M) o_j / (e^(sigma_h - M) + sum_j l_j e^(m_j - M)).
+ * bf16 output only. Other arguments as in xs_paged_attn_reduce.
+ */
+int xs_paged_attn_reduce_sinks(const float* part_o, const float* part_m, const float* part_l,
+                               const int32_t* context_lens, const void* sinks, int window_size,
+                               void* out, int batch, int num_q_heads, int head_dim,
+                               int partition_size, int max_partitions, int dtype, void* stream);
+
+/*
  * Log-sum-exp merge of split-K partitions (not on the pages: the exact identity of the
  * unsplit softmax). For each (b, h), with n = min(ceil(L_b / P), max_partitions),
  *   M = max_j m_j,  w_j = l_j exp(m_j - M),  out[b, h, :] = sum_j w_j o_j / sum_j w_j.

@@ -17,7 +17,9 @@ from ._binding import (  # noqa: F401
     xs_paged_attn_balanced_workspace_size,
     xs_paged_attn_decode_append,
     xs_paged_attn_decode_balanced,
+    xs_paged_attn_decode_sinks,
     xs_paged_attn_reduce,
+    xs_paged_attn_reduce_sinks,
     xs_stream_read_probe,
     xs_version,
 )

@@ -43,6 +43,9 @@ SIGNATURES = {
     "xs_paged_attn_decode_balanced": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, ctypes.c_size_t,
                                       _i, _i, _i, _i, _i, _i, _i, _i, _vp],
     "xs_paged_attn_balanced_workspace_size": [_i, _i, _i, _i],
+    "xs_paged_attn_decode_sinks": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _f, _vp, _vp, _vp, _vp,
+                                   _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp],
+    "xs_paged_attn_reduce_sinks": [_vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _vp],
     "xs_stream_read_probe": [_vp, ctypes.c_size_t, _vp, _i, _vp],
     "xs_last_error": [],
     "xs_version": [],
@@ -234,6 +237,49 @@ def xs_paged_attn_decode_balanced(q: torch.Tensor, k_cache: torch.Tensor, v_cach
         _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         float(scale), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), B, Hq, Hkv, D, BS,
         block_tables.shape[1], NB, _dtype_code(q), _stream_handle(stream)))
+
+
+def xs_paged_attn_decode_sinks(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                               block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                               sinks: Optional[torch.Tensor] = None, window_size: int = 0,
+                               out: Optional[torch.Tensor] = None, part_o: Optional[torch.Tensor] = None,
+                               part_m: Optional[torch.Tensor] = None, part_l: Optional[torch.Tensor] = None,
+                               partition_size: int = 0, k_new: Optional[torch.Tensor] = None,
+                               v_new: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Decode attention with per-head sinks (bf16 [Hq] or None) and a sliding window (0: none),
+    plus the fused append when k_new/v_new are given."""
+    B, Hq, Hkv, D, BS, NB, NP = _decode_common(q, k_cache, v_cache, block_tables, context_lens, out, part_o,
+                                               part_m, part_l, partition_size)
+    _dev(sinks, k_new, v_new)
+    if sinks is not None:
+        _need(sinks.shape == (Hq,) and sinks.dtype == torch.bfloat16, "sinks must be bfloat16 [num_q_heads]")
+    if k_new is not None or v_new is not None:
+        _need(k_new is not None and v_new is not None, "give both k_new and v_new, or neither")
+        _need(k_new.shape == (B, Hkv, D) and v_new.shape == (B, Hkv, D), "k_new/v_new must be [batch, Hkv, D]")
+        _need(k_new.dtype == q.dtype and v_new.dtype == q.dtype, "k_new/v_new dtype differs from q")
+    lib = load_library()
+    _check("xs_paged_attn_decode_sinks", lib.xs_paged_attn_decode_sinks(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        _ptr(sinks), int(window_size), float(scale), _ptr(out), _ptr(part_o), _ptr(part_m), _ptr(part_l),
+        B, Hq, Hkv, D, BS, block_tables.shape[1], NB, int(partition_size), NP, _dtype_code(q),
+        _stream_handle(stream)))
+
+
+def xs_paged_attn_reduce_sinks(part_o: torch.Tensor, part_m: torch.Tensor, part_l: torch.Tensor,
+                               context_lens: torch.Tensor, out: torch.Tensor, partition_size: int,
+                               sinks: Optional[torch.Tensor] = None, window_size: int = 0, stream=None) -> None:
+    """The merge of xs_paged_attn_decode_sinks' partials (same sinks and window)."""
+    _dev(part_o, part_m, part_l, context_lens, out, sinks)
+    B, Hq, NP, D = part_o.shape
+    _need(part_m.shape == (B, Hq, NP) and part_l.shape == (B, Hq, NP), "partial shapes differ")
+    _need(out.shape == (B, Hq, D), "out must be [B, Hq, D]")
+    _need(context_lens.dtype == torch.int32 and context_lens.shape == (B,), "context_lens must be int32 [batch]")
+    if sinks is not None:
+        _need(sinks.shape == (Hq,) and sinks.dtype == torch.bfloat16, "sinks must be bfloat16 [num_q_heads]")
+    lib = load_library()
+    _check("xs_paged_attn_reduce_sinks", lib.xs_paged_attn_reduce_sinks(
+        _ptr(part_o), _ptr(part_m), _ptr(part_l), _ptr(context_lens), _ptr(sinks), int(window_size), _ptr(out),
+        B, Hq, D, int(partition_size), NP, _dtype_code(out), _stream_handle(stream)))
 
 
 def xs_stream_read_probe(buf: torch.Tensor, sink: torch.Tensor, nontemporal: bool = True, stream=None) -> None:

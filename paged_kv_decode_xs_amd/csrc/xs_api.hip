@@ -193,6 +193,58 @@ XS_API int xs_paged_attn_decode_append(const void* q, const void* k_new, const v
   return launch_status(who, xs::launch_paged_decode(a, static_cast<hipStream_t>(stream)));
 }
 
+XS_API int xs_paged_attn_decode_sinks(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                      void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                                      const void* sinks, int window_size, float scale, void* out, float* part_o,
+                                      float* part_m, float* part_l, int batch, int num_q_heads, int num_kv_heads,
+                                      int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
+                                      int partition_size, int max_partitions, int dtype, void* stream) {
+  const char* who = "xs_paged_attn_decode_sinks";
+  xs::DecodeArgs a = decode_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out, part_o,
+                                 part_m, part_l, batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                                 max_blocks_per_seq, num_blocks, partition_size, max_partitions, dtype);
+  a.sinks = sinks;
+  a.window = window_size;
+  const int st = check_decode(who, a, dtype);
+  if (st != XS_OK) return st;
+  if (dtype != XS_BF16) return fail(XS_EUNSUPPORTED, "%s: sinks and windows need dtype XS_BF16", who);
+  if (!xs::mfma_decode_supported(true, head_dim, block_size))
+    return fail(XS_EUNSUPPORTED, "%s: block_size = %d (supported with sinks and windows: 16, 32)", who, block_size);
+  if (window_size < 0) return fail(XS_EINVAL, "%s: window_size = %d < 0", who, window_size);
+  if (batch == 0) return ok();
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(XS_EINVAL, "%s: k_new and v_new must both be given (fused append) or both be NULL", who);
+  if (k_new && (!aligned16(k_new) || !aligned16(v_new)))
+    return fail(XS_EINVAL, "%s: k_new and v_new must be 16-byte aligned", who);
+  if (sinks && (reinterpret_cast<uintptr_t>(sinks) & 1u)) return fail(XS_EINVAL, "%s: sinks must be 2-byte aligned", who);
+  (void)hipGetLastError();
+  return launch_status(who, xs::launch_paged_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+XS_API int xs_paged_attn_reduce_sinks(const float* part_o, const float* part_m, const float* part_l,
+                                      const int32_t* context_lens, const void* sinks, int window_size, void* out,
+                                      int batch, int num_q_heads, int head_dim, int partition_size,
+                                      int max_partitions, int dtype, void* stream) {
+  const char* who = "xs_paged_attn_reduce_sinks";
+  if (batch < 0) return fail(XS_EINVAL, "%s: batch = %d < 0", who, batch);
+  if (num_q_heads < 1) return fail(XS_EINVAL, "%s: num_q_heads = %d < 1", who, num_q_heads);
+  if (dtype != XS_BF16) return fail(XS_EUNSUPPORTED, "%s: sinks and windows need dtype XS_BF16", who);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(XS_EUNSUPPORTED, "%s: head_dim = %d (supported: 64, 128)", who, head_dim);
+  if (partition_size < 1) return fail(XS_EINVAL, "%s: partition_size = %d < 1", who, partition_size);
+  if (max_partitions < 1) return fail(XS_EINVAL, "%s: max_partitions = %d < 1", who, max_partitions);
+  if (window_size < 0) return fail(XS_EINVAL, "%s: window_size = %d < 0", who, window_size);
+  if ((long long)batch * num_q_heads > 0x7fffffffLL) return fail(XS_EINVAL, "%s: batch * num_q_heads too large", who);
+  if (batch == 0) return ok();
+  if (!part_o || !part_m || !part_l || !context_lens || !out)
+    return fail(XS_EINVAL, "%s: a required pointer is NULL", who);
+  if (sinks && (reinterpret_cast<uintptr_t>(sinks) & 1u)) return fail(XS_EINVAL, "%s: sinks must be 2-byte aligned", who);
+  (void)hipGetLastError();
+  return launch_status(who, xs::launch_paged_reduce_sinks(part_o, part_m, part_l, context_lens, sinks, window_size, out,
+                                                          batch, num_q_heads, head_dim, partition_size,
+                                                          max_partitions, true, static_cast<hipStream_t>(stream)));
+}
+
 XS_API int xs_paged_attn_reduce(const float* part_o, const float* part_m, const float* part_l,
                                 const int32_t* context_lens, void* out, int batch, int num_q_heads, int head_dim,
                                 int partition_size, int max_partitions, int dtype, void* stream) {

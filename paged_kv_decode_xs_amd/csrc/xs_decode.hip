@@ -349,6 +349,8 @@ DecodeParams make_params(const DecodeArgs& a, int heads_per_wave) {
   p.k_cache_w = static_cast<uint4*>(a.k_cache);
   p.v_cache_w = static_cast<uint4*>(a.v_cache);
   p.scale_log2e = a.scale * kLog2e;
+  p.sinks = static_cast<const uint16_t*>(a.sinks);
+  p.window = a.window;
   p.out = a.out;
   p.part_o = a.part_o;
   p.part_m = a.part_m;
@@ -366,6 +368,7 @@ DecodeParams make_params(const DecodeArgs& a, int heads_per_wave) {
 
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
   if (mfma_decode_supported(a.bf16, a.head_dim, a.block_size)) return launch_paged_decode_mfma(a, stream);
+  if (a.sinks || a.window > 0) return hipErrorInvalidValue;  // sinks and windows: matrix-core shapes only
   const int gc = heads_per_chunk(a.num_q_heads / a.num_kv_heads);
   if (a.bf16) {
     if (a.head_dim == 64) return launch_bs<true, 64>(gc, a, stream);

@@ -10,6 +10,10 @@
 // Fused append (k_new non-null): every wavefront that loads the tile holding token L-1 takes
 // that token's K/V from k_new/v_new, and one wavefront writes them into the pools; no
 // wavefront reads the slot being written.
+// SW instances add the pages' sinks and sliding window (xserv compare phase10...cf1e9e41,
+// attention.rs, `paged_decode_attention_sinks`): the range starts at position
+// max(0, L - window), whose block and tile come first, and the unsplit output takes each head's
+// sink logit into its softmax denominator. Split partials carry no sink; the sink merge adds it.
 #include "xs_internal.h"
 #include "xs_mfma_tile.h"
 
@@ -21,7 +25,7 @@ namespace {
 #endif
 
 
-template <int D, int BS, int GC, int NW>
+template <int D, int BS, int GC, int NW, bool SW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(XS_DECODE_MIN_WAVES_PER_EU)))
 void paged_decode_mfma_kernel(const DecodeParams prm) {
   using TA = TileAttn<D, GC>;
@@ -62,11 +66,14 @@ void paged_decode_mfma_kernel(const DecodeParams prm) {
   const int L = min(L_in, max_blocks_per_seq * BS);
   const int nblk_seq = L > 0 ? (L + BS - 1) / BS : 0;
   int jb = 0, je = nblk_seq;
+  // First position in the window (0 without one); blocks wholly before it are skipped.
+  const int t0w = SW && prm.window > 0 ? max(0, L - prm.window) : 0;
   if (split) {
     jb = p * prm.part_blocks;
     je = min(jb + prm.part_blocks, nblk_seq);
-    if (jb >= je) return;  // the whole workgroup leaves together
   }
+  if constexpr (SW) jb = max(jb, t0w / BS);
+  if (split && jb >= je) return;  // the whole workgroup leaves together
   const size_t q_row0 = (size_t)b * prm.num_q_heads + h0;
   if (jb >= je) {  // no split, empty context
     if (wave == 0 && lane < GC * ROW16)
@@ -117,7 +124,7 @@ void paged_decode_mfma_kernel(const DecodeParams prm) {
   // Tiles of the range, dealt round-robin to the NW wavefronts; the next tile of a wavefront is
   // loaded (into the other register set) while the current one is processed.
   const int t_end = (min(je * BS, L) + 15) / 16;
-  int t = jb * TPB + wave;
+  int t = (SW ? max(jb * TPB, t0w / 16) : jb * TPB) + wave;
   uint4 kA[KK], vA[VL], kB[KK], vB[VL];
   int bA = -1, bB = -1;
   if (t < t_end) {
@@ -130,14 +137,14 @@ void paged_decode_mfma_kernel(const DecodeParams prm) {
       bB = block_of(t2);
       if (valid(bB)) load(bB, t2, kB, vB);
     }
-    if (valid(bA)) st.process(kA, vA, min(16, L - 16 * t), vlds, prm.scale_log2e, lane);
+    if (valid(bA)) st.process_range(kA, vA, SW ? t0w - 16 * t : 0, min(16, L - 16 * t), vlds, prm.scale_log2e, lane);
     if (t2 >= t_end) break;
     const int t3 = t2 + NW;
     if (t3 < t_end) {
       bA = block_of(t3);
       if (valid(bA)) load(bA, t3, kA, vA);
     }
-    if (valid(bB)) st.process(kB, vB, min(16, L - 16 * t2), vlds, prm.scale_log2e, lane);
+    if (valid(bB)) st.process_range(kB, vB, SW ? t0w - 16 * t2 : 0, min(16, L - 16 * t2), vlds, prm.scale_log2e, lane);
     t = t3;
   }
 
@@ -203,15 +210,24 @@ void paged_decode_mfma_kernel(const DecodeParams prm) {
         prm.part_l[prow] = l_h[r];
       }
     } else {
+      float f = inv;
+      if (SW && prm.sinks) {
+        // The sink sigma (scaled-score units) joins the denominator: o = acc e^(m-M) / (l e^(m-M) + e^(sigma-M)).
+        const float sg = bf16lo_to_f32((uint32_t)prm.sinks[h0 + r]) * kLog2e;
+        const float M = fmaxf(m_h[r], sg);
+        const float fo = m_h[r] == kNegInf ? 0.f : fast_exp2(m_h[r] - M);
+        const float den = l_h[r] * fo + (sg == kNegInf ? 0.f : fast_exp2(sg - M));
+        f = den > 0.f ? fo / den : 0.f;
+      }
       uint16_t* o = reinterpret_cast<uint16_t*>(prm.out) + (q_row0 + r) * D;
 #pragma unroll
-      for (int hf = 0; hf < NH; ++hf) o[64 * hf + lane] = (uint16_t)f32_to_bf16_rne(st.acc[hp * NH + hf][i] * inv);
+      for (int hf = 0; hf < NH; ++hf) o[64 * hf + lane] = (uint16_t)f32_to_bf16_rne(st.acc[hp * NH + hf][i] * f);
     }
   }
 }
 
-template <int D, int BS, int GC>
-hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+template <int D, int BS, int GC, bool SW>
+hipError_t launch_sw(const DecodeArgs& a, hipStream_t stream) {
   const DecodeParams prm = make_params(a, GC);
   const long long np = prm.part_blocks > 0 ? a.max_partitions : 1;
   const long long grid = (long long)a.batch * a.num_kv_heads * prm.chunks * np;
@@ -222,11 +238,17 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   if (grid <= resident) nw = grid * 4 <= resident ? 4 : grid * 2 <= resident ? 2 : 1;
   const dim3 g3((unsigned)grid);
   switch (nw) {
-    case 1: hipLaunchKernelGGL((paged_decode_mfma_kernel<D, BS, GC, 1>), g3, dim3(64), 0, stream, prm); break;
-    case 2: hipLaunchKernelGGL((paged_decode_mfma_kernel<D, BS, GC, 2>), g3, dim3(128), 0, stream, prm); break;
-    default: hipLaunchKernelGGL((paged_decode_mfma_kernel<D, BS, GC, 4>), g3, dim3(256), 0, stream, prm); break;
+    case 1: hipLaunchKernelGGL((paged_decode_mfma_kernel<D, BS, GC, 1, SW>), g3, dim3(64), 0, stream, prm); break;
+    case 2: hipLaunchKernelGGL((paged_decode_mfma_kernel<D, BS, GC, 2, SW>), g3, dim3(128), 0, stream, prm); break;
+    default: hipLaunchKernelGGL((paged_decode_mfma_kernel<D, BS, GC, 4, SW>), g3, dim3(256), 0, stream, prm); break;
   }
   return hipGetLastError();
+}
+
+template <int D, int BS, int GC>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+  if (a.sinks || a.window > 0) return launch_sw<D, BS, GC, true>(a, stream);
+  return launch_sw<D, BS, GC, false>(a, stream);
 }
 
 template <int D, int BS>

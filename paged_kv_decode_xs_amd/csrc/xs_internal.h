@@ -26,6 +26,8 @@ struct DecodeArgs {
   int batch, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks;
   int partition_size, max_partitions;
   bool bf16;
+  const void* sinks = nullptr;  // bf16 [num_q_heads] sink logits, or null
+  int window = 0;               // > 0: attend to the last `window` positions only
 };
 
 // What one decode kernel receives (by value, in the kernel argument segment).
@@ -45,6 +47,8 @@ struct DecodeParams {
   float* part_m;
   float* part_l;
   int num_q_heads, num_kv_heads, group, chunks, max_blocks_per_seq, num_blocks, part_blocks, max_partitions;
+  const uint16_t* sinks;  // bf16 sink logit per query head, or null
+  int window;             // 0: all positions
 };
 
 DecodeParams make_params(const DecodeArgs& a, int heads_per_wave);
@@ -80,6 +84,13 @@ hipError_t launch_paged_reduce(const float* part_o, const float* part_m, const f
                                const int32_t* context_lens, void* out, int batch, int num_q_heads,
                                int head_dim, int partition_size, int max_partitions, bool bf16,
                                hipStream_t stream);
+
+// The merge with per-head sinks (bf16, or null) and a sliding window (0: none): partitions
+// before the window start are skipped and the sink joins the denominator once.
+hipError_t launch_paged_reduce_sinks(const float* part_o, const float* part_m, const float* part_l,
+                                     const int32_t* context_lens, const void* sinks, int window, void* out,
+                                     int batch, int num_q_heads, int head_dim, int partition_size,
+                                     int max_partitions, bool bf16, hipStream_t stream);
 
 // Matrix-core variant, for the shapes mfma_decode_supported accepts.
 bool mfma_decode_supported(bool bf16, int head_dim, int block_size);

@@ -20,8 +20,8 @@
 //       one d per lane, so V goes through the wavefront's own LDS slice and comes back 2 bytes
 //       at a time; lane l reads column d = 64h + l, 128 consecutive bytes per wavefront.
 //       The accumulator is O[head][64h + lane]: D/16 registers per 4 heads.
-// Tokens at or past the tile's valid count get score -inf and a zeroed V, so pool tails (NaN
-// included) never reach the result.
+// Tokens outside the tile's valid range get score -inf and a zeroed V, so pool tails (NaN
+// included) and positions before a sliding window never reach the result.
 #pragma once
 
 #include <math.h>
@@ -112,16 +112,23 @@ struct TileAttn {
     }
   }
 
+  // Adds the tile's tokens 0 .. nvalid-1.
   __device__ __forceinline__ void process(const uint4 (&kr)[KK], const uint4 (&vr)[VL], int nvalid,
                                           unsigned char* vlds, float scale_log2e, int lane) {
+    process_range(kr, vr, 0, nvalid, vlds, scale_log2e, lane);
+  }
+
+  // Adds the tile's tokens lo .. hi-1 (a sliding window can start inside a tile).
+  __device__ __forceinline__ void process_range(const uint4 (&kr)[KK], const uint4 (&vr)[VL], int lo, int hi,
+                                                unsigned char* vlds, float scale_log2e, int lane) {
     constexpr float kNegInf = -INFINITY;
     const int j = lane >> 4;
-    // Stage V in LDS (rows of 2D bytes); tokens at or past nvalid become zeros.
+    // Stage V in LDS (rows of 2D bytes); tokens outside [lo, hi) become zeros.
 #pragma unroll
     for (int r = 0; r < VL; ++r) {
       const int piece = r * 64 + lane;
       uint4 v = vr[r];
-      if (piece / ROW16 >= nvalid) v = make_uint4(0, 0, 0, 0);
+      if (piece / ROW16 >= hi || piece / ROW16 < lo) v = make_uint4(0, 0, 0, 0);
       reinterpret_cast<uint4*>(vlds)[piece] = v;
     }
     // QK on the matrix cores.
@@ -133,7 +140,7 @@ struct TileAttn {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       sc[i] = s[i] * scale_log2e;
-      if (4 * j + i >= nvalid) sc[i] = kNegInf;
+      if (4 * j + i >= hi || 4 * j + i < lo) sc[i] = kNegInf;
     }
     float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));

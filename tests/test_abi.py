@@ -152,3 +152,45 @@ def test_decode_append_rejects_missing_new_rows():
     args[0] = None  # q
     assert lib.xs_paged_attn_decode_append(*args) == 1
     assert "NULL" in xb.xs_last_error()
+
+
+def _decode_sinks(**kw):
+    a = dict(q=FAKE, kn=None, vn=None, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, sinks=FAKE, w=0, scale=0.125, out=FAKE,
+             po=None, pm=None, pl=None, batch=2, hq=8, hkv=2, d=128, bs=16, mbps=4, nb=16, p=0, np_=0, dt=B,
+             stream=None)
+    a.update(kw)
+    return xb.load_library().xs_paged_attn_decode_sinks(
+        a["q"], a["kn"], a["vn"], a["k"], a["v"], a["bt"], a["cl"], a["sinks"], a["w"], a["scale"], a["out"],
+        a["po"], a["pm"], a["pl"], a["batch"], a["hq"], a["hkv"], a["d"], a["bs"], a["mbps"], a["nb"], a["p"],
+        a["np_"], a["dt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dt=F), 2, "XS_BF16"),
+    (dict(bs=8), 2, "block_size"),
+    (dict(w=-1), 1, "window_size"),
+    (dict(kn=FAKE), 1, "both"),
+    (dict(sinks=FAKE + 1), 1, "2-byte"),
+    (dict(hq=6, hkv=4), 1, "multiple"),
+    (dict(p=24, np_=2, po=FAKE, pm=FAKE, pl=FAKE, out=None), 1, "multiple of block_size"),
+])
+def test_decode_sinks_rejects(kw, status, needle):
+    assert _decode_sinks(**kw) == status
+    assert needle in xb.xs_last_error()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dt=F), 2, "XS_BF16"),
+    (dict(w=-3), 1, "window_size"),
+    (dict(pm=None), 1, "NULL"),
+    (dict(d=96), 2, "head_dim"),
+])
+def test_reduce_sinks_rejects(kw, status, needle):
+    a = dict(po=FAKE, pm=FAKE, pl=FAKE, cl=FAKE, sinks=None, w=0, out=FAKE, batch=2, hq=4, d=64, p=16, np_=3, dt=B,
+             stream=None)
+    a.update(kw)
+    st = xb.load_library().xs_paged_attn_reduce_sinks(a["po"], a["pm"], a["pl"], a["cl"], a["sinks"], a["w"],
+                                                       a["out"], a["batch"], a["hq"], a["d"], a["p"], a["np_"],
+                                                       a["dt"], a["stream"])
+    assert st == status
+    assert needle in xb.xs_last_error()

@@ -32,7 +32,9 @@ Recipe (the same for every workload):
    The "rmsnorm_gain" rows: z ~ N(0,1) per row of D in fp64, x = z / rms(z),
    times a gain vector of shape [D] drawn from N(1, 0.1) once per tensor kind
    (one for q, one for k). V stays N(0, 1).
-6. Poison: every pool slot that no sequence owns is NaN. That is all unused
+6. Sinks (workloads that have them): one N(0, 1) value per query head, drawn after
+   everything else, then rounded like the other values.
+7. Poison: every pool slot that no sequence owns is NaN. That is all unused
    blocks, the tail slots t >= L_b of each last block, and the slot L_b - 1
    itself, which the decode step's append must fill.
 
@@ -69,6 +71,8 @@ class Workload:
     values: str  # "normal" or "rmsnorm_gain"
     seed: int
     partition_size: int  # tokens per split-K partition used by the bench and tests
+    window: int = 0  # > 0: the query attends to the last `window` positions only
+    sinks: bool = False  # one attention-sink logit per query head (drawn last, N(0, 1) -> dtype)
 
     @property
     def group(self) -> int:
@@ -128,6 +132,14 @@ WORKLOADS: Dict[str, Workload] = {
             dtype="bf16", batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
             ctx=("fixed", [8192, 16384, 24576, 32768]), num_blocks=None, max_blocks_per_seq=2048,
             values="normal", seed=4, partition_size=512,
+        ),
+        Workload(
+            name="gptoss_20b_window128_b64",
+            description="gpt-oss-20b sliding-window layer shape, bf16: 64 sequences, 64 q / 8 KV heads, "
+            "head_dim 64, 128-token window, one sink per head, context_lens uniform in [128,8192]",
+            dtype="bf16", batch=64, num_q_heads=64, num_kv_heads=8, head_dim=64, block_size=16,
+            ctx=("uniform", 128, 8192), num_blocks=None, max_blocks_per_seq=512, values="normal",
+            seed=5, partition_size=0, window=128, sinks=True,
         ),
     ]
 }
@@ -191,6 +203,7 @@ class Case:
     v_cache: np.ndarray
     block_tables: np.ndarray  # int32 [B, MBPS], -1 padded
     context_lens: np.ndarray  # int32 [B], length after this step's append
+    sinks: Optional[np.ndarray] = None  # [Hq] sink logits (dtype bits), or None
 
     @property
     def num_blocks(self) -> int:
@@ -200,10 +213,16 @@ class Case:
     def scale(self) -> float:
         return self.workload.scale
 
+    def attended_tokens(self) -> int:
+        """sum_b of the positions the query sees: L_b, or min(L_b, window) with a window."""
+        L = np.maximum(self.context_lens.astype(np.int64), 0)
+        w = self.workload.window
+        return int((np.minimum(L, w) if w > 0 else L).sum())
+
     def kv_bytes(self) -> int:
-        """K+V bytes attention must stream: sum_b L_b * Hkv * D * elt * 2."""
+        """K+V bytes attention must stream: sum_b L_b * Hkv * D * elt * 2 (window-limited)."""
         w = self.workload
-        return int(self.context_lens.astype(np.int64).sum()) * w.num_kv_heads * w.head_dim * w.elt_bytes * 2
+        return self.attended_tokens() * w.num_kv_heads * w.head_dim * w.elt_bytes * 2
 
 
 @dataclasses.dataclass
@@ -283,8 +302,10 @@ def make_case(w: Workload, seed: Optional[int] = None, lens: Optional[np.ndarray
         k_cache[ids] = kb
         v_cache[ids] = vb
 
+    sinks = _encode(_normal(rng, (Hq,)), w.dtype) if w.sinks else None
     return Case(
         workload=w,
+        sinks=sinks,
         q=_encode(q, w.dtype),
         k_new=_encode(k_new, w.dtype),
         v_new=_encode(v_new, w.dtype),
