@@ -222,7 +222,11 @@ def extra_row(w, P: int, fused: bool, r) -> dict:
     case = r["case"]
     ab = algorithmic_bytes(case, P)
     decode_bytes = ab["decode"] + (ab["append"] if fused else 0)
-    achieved = decode_bytes / (r["decode_ms_mean"] * 1e-3) / 1e9
+    # A fused unsplit step is one launch: back-to-back steps time it without the few microseconds
+    # an event pair adds, which matter at this size.
+    one_launch = fused and P == 0
+    decode_ms = r["ms_step"] if one_launch else r["decode_ms_mean"]
+    achieved = decode_bytes / (decode_ms * 1e-3) / 1e9
     return {
         "workload": w.name,
         "description": w.description,
@@ -234,7 +238,8 @@ def extra_row(w, P: int, fused: bool, r) -> dict:
         "ms_per_step": round(r["ms_step"], 5),
         "kv_GBps": round(ab["kv"] / (r["ms_step"] * 1e-3) / 1e9, 2),
         "seqs_per_s": round(w.batch / (r["ms_step"] * 1e-3), 1),
-        "decode_launch_us": round(r["decode_ms_mean"] * 1e3, 2),
+        "decode_launch_us": round(decode_ms * 1e3, 2),
+        "decode_timing": "back-to-back steps (one launch per step)" if one_launch else "HIP events around each launch",
         "decode_algorithmic_GBps": round(achieved, 2),
         "decode_frac_of_hbm_peak": round(achieved / HBM_PEAK_GBS, 4),
     }
