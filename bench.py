@@ -217,6 +217,77 @@ def run_workload(w, P: int, fused: bool, K: int, warmup: int, copies=None):
     return {"case": case, "R": R, "ms_step": ms_step, "decode_ms_mean": decode_ms_mean, "out": out}
 
 
+# Launch-bound workloads timed eagerly and as a replayed HIP graph (xs_step_graph_*), as a stack of
+# decode steps, one per layer of the model (GPT-2 124M: 12 layers; Qwen3-8B: 36).
+GRAPH_WORKLOADS = [("gpt2_fp32_ctx32", 12), ("gpt2_bf16_b8", 12), ("qwen3_8b_b1_ctx4096", 36)]
+
+
+def graph_row(w, layers: int, K: int, warmup: int) -> dict:
+    """Eager decode steps vs the same steps replayed as one HIP graph: `layers` steps per token, each
+    on its own K/V pools. One resident set of pools (a graph replays fixed addresses), so this row is
+    warm-cache. GPU time: HIP events around K tokens; host time: wall time to issue K tokens and
+    wait for them. Both are reported per layer step."""
+    import torch
+
+    import paged_kv_decode_xs_amd as xs
+    import workloads as wl
+    from workloads.device import case_to_device
+
+    case = wl.make_case(w)
+    dev = case_to_device(case, "cuda:0")
+    P = w.partition_size
+    steps = []
+    for i in range(layers):
+        kc, vc = (dev["k_cache"], dev["v_cache"]) if i == 0 else (dev["k_cache"].clone(), dev["v_cache"].clone())
+        steps.append(xs.DecodeStep(dev["q"], kc, vc, dev["block_tables"], dev["context_lens"], dev["k_new"],
+                                   dev["v_new"], w.scale, partition_size=P,
+                                   max_context_len=int(case.context_lens.max()), fused=True))
+    stream = torch.cuda.current_stream()
+
+    def eager():
+        for s in steps:
+            s.run(stream)
+
+    for _ in range(warmup):
+        eager()
+    torch.cuda.synchronize()
+    graph = xs.StepGraph(steps)
+    for _ in range(warmup):
+        graph.launch(stream)
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        a.record(stream)
+        for _ in range(K):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        host = (time.perf_counter() - t0) / (K * layers)
+        return a.elapsed_time(b) / (K * layers), host
+
+    eager_ms, eager_host = timed(eager)
+    graph_ms, graph_host = timed(lambda: graph.launch(stream))
+    graph.close()
+    kv = case.kv_bytes()
+    return {
+        "workload": w.name,
+        "layers_per_token": layers,
+        "partition_size": P,
+        "kernels_per_layer_step": 2 if P > 0 else 1,
+        "kv_bytes_per_layer_step": kv,
+        "eager_us_per_layer_step": round(eager_ms * 1e3, 2),
+        "graph_us_per_layer_step": round(graph_ms * 1e3, 2),
+        "eager_host_us_per_layer_step": round(eager_host * 1e6, 2),
+        "graph_host_us_per_layer_step": round(graph_host * 1e6, 2),
+        "graph_speedup": round(eager_ms / graph_ms, 2),
+        "graph_kv_GBps": round(kv / (graph_ms * 1e-3) / 1e9, 2),
+        "cache": "warm (resident pools: the graph replays fixed addresses)",
+    }
+
+
 def extra_row(w, P: int, fused: bool, r) -> dict:
     """One line of "extra_workloads": the same quantities as the headline, for another workload."""
     case = r["case"]
@@ -379,6 +450,8 @@ def main() -> int:
             rows.append(extra_row(we, we.partition_size, fused,
                                   run_workload(we, we.partition_size, fused, min(K, 100), args.warmup)))
         result["extra_workloads"] = rows
+        result["graph_replay"] = [graph_row(wl.WORKLOADS[name], layers, min(K, 50), min(args.warmup, 5))
+                                  for name, layers in GRAPH_WORKLOADS]
     print(json.dumps(result), flush=True)
     return 0 if result.get("parity_vs_oracle", {}).get("out_of_tolerance", 0) == 0 else 3
 

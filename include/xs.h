@@ -200,6 +200,58 @@ int xs_paged_attn_reduce_sinks(const float* part_o, const float* part_m, const f
                                int partition_size, int max_partitions, int dtype, void* stream);
 
 /*
+ * Decode steps as one HIP graph: captured once, then replayed (xserv compare
+ * phase10...cf1e9e41, crates/xserv-cuda/src/graph.rs: capture a fixed sequence of launches and
+ * replay it without per-launch host work; shapes and addresses fixed at capture, no host
+ * branching inside; the decode loop there captures the whole forward of a token, every layer).
+ * A graph holds num_steps steps in order, e.g. one per layer of a model. Each step is the append of k_new/v_new (fused into the decode when `fused` != 0,
+ * otherwise xs_kv_append's kernel first), the decode (xs_paged_attn_decode_sinks when sinks or
+ * window_size are given, else xs_paged_attn_decode), and, when partition_size > 0, the matching
+ * reduce into `out`. Fields mean what the arguments of those calls mean; all pointers are
+ * device pointers that must stay valid while the graph exists. Their contents (q, k_new,
+ * v_new, block_tables, context_lens, sinks) may change between replays: a decode loop updates
+ * them in place and replays. Sizes (batch, max_partitions, ...) are fixed at capture.
+ */
+typedef struct {
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const void* sinks;  /* NULL: no sinks */
+  int window_size;    /* 0: no window */
+  float scale;
+  void* out;
+  float* part_o;      /* split-K partials: NULL when partition_size == 0 */
+  float* part_m;
+  float* part_l;
+  int batch, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks;
+  int partition_size, max_partitions, dtype;
+  int fused;          /* != 0: append fused into the decode launch */
+} xs_step_desc;
+
+typedef struct xs_step_graph xs_step_graph;
+
+/*
+ * Checks descs[0 .. num_steps-1] (1 <= num_steps <= 4096), each as the entry points above check
+ * their arguments, plus: batch >= 1, k_new and v_new given; then captures the steps in order on a
+ * private stream and instantiates the graph. On success
+ * *out_graph owns a HIP graph and its executable instance (host-side runtime objects; no device
+ * memory is allocated by this library). On failure *out_graph is NULL. Capture runs in
+ * thread-local mode: other threads may keep using HIP meanwhile.
+ */
+int xs_step_graph_create(const xs_step_desc* descs, int num_steps, xs_step_graph** out_graph);
+
+/* Replays the captured steps on `stream` (asynchronous, like the calls above). */
+int xs_step_graph_launch(xs_step_graph* graph, void* stream);
+
+/* Releases the graph (NULL is a no-op). The caller must not destroy a graph that is still
+ * running on a stream. */
+int xs_step_graph_destroy(xs_step_graph* graph);
+
+/*
  * Log-sum-exp merge of split-K partitions (not on the pages: the exact identity of the
  * unsplit softmax). For each (b, h), with n = min(ceil(L_b / P), max_partitions),
  *   M = max_j m_j,  w_j = l_j exp(m_j - M),  out[b, h, :] = sum_j w_j o_j / sum_j w_j.

@@ -20,7 +20,10 @@ from ._binding import (  # noqa: F401
     xs_paged_attn_decode_sinks,
     xs_paged_attn_reduce,
     xs_paged_attn_reduce_sinks,
+    xs_step_graph_create,
+    xs_step_graph_destroy,
+    xs_step_graph_launch,
     xs_stream_read_probe,
     xs_version,
 )
-from .step import DecodeStep  # noqa: F401
+from .step import DecodeStep, StepGraph  # noqa: F401

@@ -33,6 +33,22 @@ _vp = ctypes.c_void_p
 _i = ctypes.c_int
 _f = ctypes.c_float
 
+class XsStepDesc(ctypes.Structure):
+    """Mirror of xs_step_desc in include/xs.h (field order and types must match)."""
+
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
+        ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("block_tables", ctypes.c_void_p),
+        ("context_lens", ctypes.c_void_p), ("sinks", ctypes.c_void_p), ("window_size", ctypes.c_int),
+        ("scale", ctypes.c_float), ("out", ctypes.c_void_p), ("part_o", ctypes.c_void_p),
+        ("part_m", ctypes.c_void_p), ("part_l", ctypes.c_void_p), ("batch", ctypes.c_int),
+        ("num_q_heads", ctypes.c_int), ("num_kv_heads", ctypes.c_int), ("head_dim", ctypes.c_int),
+        ("block_size", ctypes.c_int), ("max_blocks_per_seq", ctypes.c_int), ("num_blocks", ctypes.c_int),
+        ("partition_size", ctypes.c_int), ("max_partitions", ctypes.c_int), ("dtype", ctypes.c_int),
+        ("fused", ctypes.c_int),
+    ]
+
+
 SIGNATURES = {
     "xs_kv_append": [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp],
     "xs_paged_attn_decode": [_vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _vp,
@@ -47,6 +63,9 @@ SIGNATURES = {
                                    _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp],
     "xs_paged_attn_reduce_sinks": [_vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _vp],
     "xs_stream_read_probe": [_vp, ctypes.c_size_t, _vp, _i, _vp],
+    "xs_step_graph_create": [ctypes.POINTER(XsStepDesc), _i, ctypes.POINTER(ctypes.c_void_p)],
+    "xs_step_graph_launch": [_vp, _vp],
+    "xs_step_graph_destroy": [_vp],
     "xs_last_error": [],
     "xs_version": [],
 }
@@ -289,6 +308,22 @@ def xs_stream_read_probe(buf: torch.Tensor, sink: torch.Tensor, nontemporal: boo
     _need(sink.numel() * sink.element_size() >= 4, "sink must hold 4 bytes")
     _check("xs_stream_read_probe", load_library().xs_stream_read_probe(
         _ptr(buf), nbytes - nbytes % 16, _ptr(sink), int(bool(nontemporal)), _stream_handle(stream)))
+
+
+def xs_step_graph_create(descs) -> int:
+    """Capture decode steps (a sequence of XsStepDesc, run in order) as one HIP graph; returns the handle."""
+    arr = (XsStepDesc * len(descs))(*descs)
+    handle = ctypes.c_void_p()
+    _check("xs_step_graph_create", load_library().xs_step_graph_create(arr, len(descs), ctypes.byref(handle)))
+    return handle.value
+
+
+def xs_step_graph_launch(handle: int, stream=None) -> None:
+    _check("xs_step_graph_launch", load_library().xs_step_graph_launch(handle, _stream_handle(stream)))
+
+
+def xs_step_graph_destroy(handle: int) -> None:
+    _check("xs_step_graph_destroy", load_library().xs_step_graph_destroy(handle))
 
 
 def num_partitions(max_context_len: int, partition_size: int) -> int:

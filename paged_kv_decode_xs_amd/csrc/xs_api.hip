@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include <string>
+#include <vector>
 
 #include "xs.h"
 #include "xs_internal.h"
@@ -305,4 +306,129 @@ XS_API int xs_stream_read_probe(const void* buf, size_t bytes, unsigned* sink, i
   if (bytes == 0) return ok();
   (void)hipGetLastError();
   return launch_status(who, xs::launch_stream_read(buf, bytes, sink, nontemporal != 0, static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------------------------------------
+// Decode step as one HIP graph (captured once, replayed per step).
+
+struct xs_step_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+namespace {
+
+// Enqueues one decode step on `s`: the append (fused into the decode, or its own kernel), the
+// decode, and the reduce when split. The arguments were checked by the caller.
+hipError_t enqueue_step(const xs::DecodeArgs& a, const xs_step_desc* d, hipStream_t s) {
+  hipError_t e;
+  const bool sw = a.sinks != nullptr || a.window > 0;
+  if (d->fused) {
+    e = xs::launch_paged_decode(a, s);
+  } else {
+    e = xs::launch_kv_append(d->k_new, d->v_new, d->k_cache, d->v_cache, d->block_tables, d->context_lens, d->batch,
+                             d->num_kv_heads, d->head_dim, d->block_size, d->max_blocks_per_seq, d->num_blocks,
+                             elt_bytes(d->dtype), s);
+    if (e != hipSuccess) return e;
+    xs::DecodeArgs b = a;
+    b.k_new = b.v_new = nullptr;
+    e = xs::launch_paged_decode(b, s);
+  }
+  if (e != hipSuccess || a.partition_size == 0) return e;
+  if (sw)
+    return xs::launch_paged_reduce_sinks(a.part_o, a.part_m, a.part_l, a.context_lens, a.sinks, a.window, a.out,
+                                         a.batch, a.num_q_heads, a.head_dim, a.partition_size, a.max_partitions,
+                                         a.bf16, s);
+  return xs::launch_paged_reduce(a.part_o, a.part_m, a.part_l, a.context_lens, a.out, a.batch, a.num_q_heads,
+                                 a.head_dim, a.partition_size, a.max_partitions, a.bf16, s);
+}
+
+}  // namespace
+
+namespace {
+
+// Checks one step descriptor; builds its DecodeArgs.
+int check_step(const char* who, int idx, const xs_step_desc* d, xs::DecodeArgs* out_args) {
+  xs::DecodeArgs a = decode_args(d->q, d->k_new, d->v_new, d->k_cache, d->v_cache, d->block_tables,
+                                 d->context_lens, d->scale, d->partition_size > 0 ? nullptr : d->out, d->part_o,
+                                 d->part_m, d->part_l, d->batch, d->num_q_heads, d->num_kv_heads, d->head_dim,
+                                 d->block_size, d->max_blocks_per_seq, d->num_blocks, d->partition_size,
+                                 d->max_partitions, d->dtype);
+  a.sinks = d->sinks;
+  a.window = d->window_size;
+  int st = check_decode(who, a, d->dtype);
+  if (st != XS_OK) return st;
+  a.out = d->out;  // the reduce's output when split
+  if (d->batch < 1) return fail(XS_EINVAL, "%s: step %d: batch = %d < 1 (nothing to capture)", who, idx, d->batch);
+  if (!d->k_new || !d->v_new)
+    return fail(XS_EINVAL, "%s: step %d: the step appends: k_new and v_new are required", who, idx);
+  if (!aligned16(d->k_new) || !aligned16(d->v_new))
+    return fail(XS_EINVAL, "%s: step %d: k_new and v_new must be 16-byte aligned", who, idx);
+  if (d->partition_size > 0 && (!d->out || !aligned16(d->out)))
+    return fail(XS_EINVAL, "%s: step %d: out (the reduce's output) must be a 16-byte aligned pointer", who, idx);
+  if (d->window_size < 0) return fail(XS_EINVAL, "%s: step %d: window_size = %d < 0", who, idx, d->window_size);
+  if (d->sinks || d->window_size > 0) {
+    if (d->dtype != XS_BF16)
+      return fail(XS_EUNSUPPORTED, "%s: step %d: sinks and windows need dtype XS_BF16", who, idx);
+    if (!xs::mfma_decode_supported(true, d->head_dim, d->block_size))
+      return fail(XS_EUNSUPPORTED, "%s: step %d: block_size = %d (supported with sinks and windows: 16, 32)", who,
+                  idx, d->block_size);
+    if (d->sinks && (reinterpret_cast<uintptr_t>(d->sinks) & 1u))
+      return fail(XS_EINVAL, "%s: step %d: sinks must be 2-byte aligned", who, idx);
+  }
+  *out_args = a;
+  return XS_OK;
+}
+
+}  // namespace
+
+XS_API int xs_step_graph_create(const xs_step_desc* descs, int num_steps, xs_step_graph** out_graph) {
+  const char* who = "xs_step_graph_create";
+  if (!out_graph) return fail(XS_EINVAL, "%s: out_graph is NULL", who);
+  *out_graph = nullptr;
+  if (!descs) return fail(XS_EINVAL, "%s: descs is NULL", who);
+  if (num_steps < 1 || num_steps > 4096) return fail(XS_EINVAL, "%s: num_steps = %d (1..4096)", who, num_steps);
+  std::vector<xs::DecodeArgs> args((size_t)num_steps);
+  for (int i = 0; i < num_steps; ++i) {
+    const int st = check_step(who, i, &descs[i], &args[(size_t)i]);
+    if (st != XS_OK) return st;
+  }
+  (void)hipGetLastError();
+  hipStream_t s = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+  if (e != hipSuccess) return fail(XS_ELAUNCH, "%s: hipStreamCreateWithFlags: %s", who, hipGetErrorString(e));
+  hipGraph_t graph = nullptr;
+  e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+  if (e == hipSuccess) {
+    hipError_t le = hipSuccess;
+    for (int i = 0; i < num_steps && le == hipSuccess; ++i) le = enqueue_step(args[(size_t)i], &descs[i], s);
+    e = hipStreamEndCapture(s, &graph);  // always end the capture, even after a failed launch
+    if (le != hipSuccess) e = le;
+  }
+  hipGraphExec_t exec = nullptr;
+  if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  (void)hipStreamDestroy(s);
+  if (e != hipSuccess) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return fail(XS_ELAUNCH, "%s: capture failed: %s", who, hipGetErrorString(e));
+  }
+  *out_graph = new xs_step_graph{graph, exec};
+  return ok();
+}
+
+XS_API int xs_step_graph_launch(xs_step_graph* g, void* stream) {
+  const char* who = "xs_step_graph_launch";
+  if (!g) return fail(XS_EINVAL, "%s: graph is NULL", who);
+  (void)hipGetLastError();
+  return launch_status(who, hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream)));
+}
+
+XS_API int xs_step_graph_destroy(xs_step_graph* g) {
+  if (!g) return ok();
+  const hipError_t e1 = hipGraphExecDestroy(g->exec);
+  const hipError_t e2 = hipGraphDestroy(g->graph);
+  delete g;
+  if (e1 != hipSuccess || e2 != hipSuccess)
+    return fail(XS_ELAUNCH, "xs_step_graph_destroy: %s", hipGetErrorString(e1 != hipSuccess ? e1 : e2));
+  return ok();
 }

@@ -8,6 +8,8 @@ With schedule="balanced" the step is xs_paged_attn_decode_balanced (append inclu
 otherwise xs_kv_append first), which writes `out` itself; partition_size is then unused.
 With sinks (bf16 [Hq]) or window > 0 the decode and the reduce are xs_paged_attn_decode_sinks and
 xs_paged_attn_reduce_sinks (split schedule only).
+`DecodeStep.capture()` records the same step as one HIP graph (xs_step_graph_create); replaying it
+runs the step on the buffers as they are at replay time.
 """
 
 from __future__ import annotations
@@ -101,6 +103,10 @@ class DecodeStep:
                                          k_new=self.k_new if self.fused else None,
                                          v_new=self.v_new if self.fused else None, stream=stream)
 
+    def capture(self) -> "StepGraph":
+        """This step (split schedule) as one HIP graph."""
+        return StepGraph([self])
+
     def run(self, stream=None) -> torch.Tensor:
         if self.schedule == "balanced":
             if not self.fused:
@@ -114,3 +120,50 @@ class DecodeStep:
             self.attend(stream)
         self.reduce(stream)
         return self.out
+
+
+def _step_desc(step: "DecodeStep") -> "xb.XsStepDesc":
+    """The C descriptor of one step's buffers and sizes."""
+    q = step.q
+    B, Hq, D = q.shape
+    NB, Hkv, BS, _ = step.k_cache.shape
+    split = step.partition_size > 0
+    return xb.XsStepDesc(
+        q=q.data_ptr(), k_new=step.k_new.data_ptr(), v_new=step.v_new.data_ptr(),
+        k_cache=step.k_cache.data_ptr(), v_cache=step.v_cache.data_ptr(),
+        block_tables=step.block_tables.data_ptr(), context_lens=step.context_lens.data_ptr(),
+        sinks=None if step.sinks is None else step.sinks.data_ptr(), window_size=step.window,
+        scale=step.scale, out=step.out.data_ptr(),
+        part_o=step.part_o.data_ptr() if split else None, part_m=step.part_m.data_ptr() if split else None,
+        part_l=step.part_l.data_ptr() if split else None, batch=B, num_q_heads=Hq, num_kv_heads=Hkv,
+        head_dim=D, block_size=BS, max_blocks_per_seq=step.block_tables.shape[1], num_blocks=NB,
+        partition_size=step.partition_size, max_partitions=step.part_m.shape[-1] if split else 0,
+        dtype=xb._dtype_code(q), fused=int(step.fused))
+
+
+class StepGraph:
+    """Decode steps captured in order as one HIP graph, e.g. one per layer (owns the handle;
+    close() or garbage collection frees it)."""
+
+    def __init__(self, steps):
+        self._steps = list(steps)  # keeps the captured buffers alive
+        for s in self._steps:
+            if s.schedule != "split":
+                raise ValueError("graph capture covers the split schedule")
+        self._handle = xb.xs_step_graph_create([_step_desc(s) for s in self._steps])
+
+    def launch(self, stream=None) -> torch.Tensor:
+        """Replays the steps; returns the last step's output."""
+        xb.xs_step_graph_launch(self._handle, stream)
+        return self._steps[-1].out
+
+    def close(self) -> None:
+        if self._handle:
+            xb.xs_step_graph_destroy(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass

@@ -194,3 +194,59 @@ def test_reduce_sinks_rejects(kw, status, needle):
                                                        a["dt"], a["stream"])
     assert st == status
     assert needle in xb.xs_last_error()
+
+
+def test_step_graph_rejects_before_any_hip_call():
+    lib = xb.load_library()
+    h = ctypes.c_void_p(123)
+    assert lib.xs_step_graph_create(None, 1, ctypes.byref(h)) == 1 and "descs is NULL" in xb.xs_last_error()
+    assert h.value is None
+    d = xb.XsStepDesc(q=FAKE, k_new=FAKE, v_new=FAKE, k_cache=FAKE, v_cache=FAKE, block_tables=FAKE,
+                      context_lens=FAKE, sinks=None, window_size=0, scale=0.125, out=FAKE, part_o=None, part_m=None,
+                      part_l=None, batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                      max_blocks_per_seq=4, num_blocks=16, partition_size=0, max_partitions=0, dtype=B, fused=1)
+    for field, value, status, needle in [("k_new", None, 1, "k_new and v_new"), ("batch", 0, 1, "nothing to capture"),
+                                         ("head_dim", 96, 2, "head_dim"), ("window_size", -2, 1, "window_size"),
+                                         ("dtype", F, 2, "XS_BF16")]:
+        saved = getattr(d, field)
+        setattr(d, field, value)
+        if field == "dtype":
+            d.window_size = 8
+        assert lib.xs_step_graph_create(ctypes.byref(d), 1, ctypes.byref(h)) == status, field
+        assert needle in xb.xs_last_error(), (field, xb.xs_last_error())
+        setattr(d, field, saved)
+        d.window_size = 0
+    assert lib.xs_step_graph_launch(None, None) == 1
+    assert lib.xs_step_graph_destroy(None) == 0
+
+
+def test_step_desc_layout_matches_header():
+    # The binding's structure must match the C declaration field for field.
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct \{(.*?)\} xs_step_desc;", text, re.S).group(1)
+    names = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if not decl:
+            continue
+        head, _, rest = decl.rpartition(" ")
+        parts = [p.strip().lstrip("*") for p in decl.split(",")]
+        first = parts[0].split()[-1].lstrip("*")
+        names.append(first)
+        names.extend(p.split()[-1].lstrip("*") for p in parts[1:])
+    assert names == [f for f, _ in xb.XsStepDesc._fields_]
+
+
+def test_step_graph_rejects_step_count_and_names_the_bad_step():
+    lib = xb.load_library()
+    h = ctypes.c_void_p()
+    good = dict(q=FAKE, k_new=FAKE, v_new=FAKE, k_cache=FAKE, v_cache=FAKE, block_tables=FAKE, context_lens=FAKE,
+                sinks=None, window_size=0, scale=0.125, out=FAKE, part_o=None, part_m=None, part_l=None, batch=2,
+                num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16, max_blocks_per_seq=4, num_blocks=16,
+                partition_size=0, max_partitions=0, dtype=B, fused=1)
+    arr = (xb.XsStepDesc * 3)(xb.XsStepDesc(**good), xb.XsStepDesc(**good), xb.XsStepDesc(**dict(good, head_dim=80)))
+    assert lib.xs_step_graph_create(arr, 0, ctypes.byref(h)) == 1 and "num_steps" in xb.xs_last_error()
+    assert lib.xs_step_graph_create(arr, 3, ctypes.byref(h)) == 2 and "head_dim" in xb.xs_last_error()
+    arr[2].head_dim = 128
+    arr[1].batch = 0
+    assert lib.xs_step_graph_create(arr, 3, ctypes.byref(h)) == 1 and "step 1" in xb.xs_last_error()
