@@ -143,7 +143,7 @@ def cpu_baseline(case, gpu_out, budget_s: float):
 
 
 # Workloads measured after the headline one, each on its own line in "extra_workloads".
-EXTRA_WORKLOADS = ["gptoss_20b_window128_b64"]
+EXTRA_WORKLOADS = ["qwen3_8b_b64_tp8_share", "gptoss_20b_window128_b64"]
 
 
 def run_workload(w, P: int, fused: bool, K: int, warmup: int, copies=None):

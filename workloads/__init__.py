@@ -134,6 +134,14 @@ WORKLOADS: Dict[str, Workload] = {
             values="normal", seed=4, partition_size=512,
         ),
         Workload(
+            name="qwen3_8b_b64_tp8_share",
+            description="one GPU's share of the 64-sequence Qwen3-8B batch at tensor parallelism 8: "
+            "4 q / 1 KV head, head_dim 128, the same context_lens (uniform in [128,8192], seed 3)",
+            dtype="bf16", batch=64, num_q_heads=4, num_kv_heads=1, head_dim=128, block_size=16,
+            ctx=("uniform", 128, 8192), num_blocks=None, max_blocks_per_seq=512, values="normal",
+            seed=3, partition_size=256,
+        ),
+        Workload(
             name="gptoss_20b_window128_b64",
             description="gpt-oss-20b sliding-window layer shape, bf16: 64 sequences, 64 q / 8 KV heads, "
             "head_dim 64, 128-token window, one sink per head, context_lens uniform in [128,8192]",
