@@ -16,6 +16,8 @@ Contents:
   last position.
 * ``sinks_window``: the same decode with per-head attention sinks and a
   sliding window, unsplit and split (the sink joins once, in the merge).
+* ``swap``: KV block swap-out / swap-in between the pools and host swap space
+  (bit copies of whole blocks, list-driven).
 * ``brute_force``: the definitions again, in Python ``decimal`` at
   40 digits over flat offsets, for tiny inputs only.
 
