@@ -288,6 +288,60 @@ def graph_row(w, layers: int, K: int, warmup: int) -> dict:
     }
 
 
+def swap_row(reps: int = 10) -> dict:
+    """KV block swap over the host link: 4096 scattered blocks of the Qwen3-8B pool shape (32 KB of
+    K and 32 KB of V each, 256 MB per direction) between the pools and a pinned swap space, one
+    launch per direction, against a plain contiguous copy of the same bytes (hipMemcpyAsync through
+    torch's copy_) between device memory and pinned host memory. Median of `reps` timed runs."""
+    import torch
+
+    import paged_kv_decode_xs_amd as xs
+
+    NB, S, n, shape = 8192, 4096, 4096, (8, 16, 128)
+    g = torch.Generator(device="cuda").manual_seed(1)
+    kc = torch.randint(-32768, 32767, (NB,) + shape, dtype=torch.int16, device="cuda", generator=g).view(torch.bfloat16)
+    vc = torch.randint(-32768, 32767, (NB,) + shape, dtype=torch.int16, device="cuda", generator=g).view(torch.bfloat16)
+    kh = torch.empty((S,) + shape, dtype=torch.bfloat16, pin_memory=True)
+    vh = torch.empty((S,) + shape, dtype=torch.bfloat16, pin_memory=True)
+    rng = np.random.default_rng(2)
+    blocks = torch.from_numpy(rng.choice(NB, n, replace=False).astype(np.int32)).cuda()
+    slots = torch.from_numpy(rng.permutation(S)[:n].astype(np.int32)).cuda()
+    nbytes = 2 * n * kc[0].numel() * kc.element_size()
+    stream = torch.cuda.current_stream()
+
+    def med(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    out_ms = med(lambda: xs.xs_kv_swap_out(kc, vc, kh, vh, blocks, slots, stream=stream))
+    in_ms = med(lambda: xs.xs_kv_swap_in(kh, vh, kc, vc, slots, blocks, stream=stream))
+    dev_flat = kc[:2 * n].reshape(-1)
+    host_flat = torch.empty(dev_flat.shape, dtype=dev_flat.dtype, pin_memory=True)
+    d2h_ms = med(lambda: host_flat.copy_(dev_flat, non_blocking=True))
+    h2d_ms = med(lambda: dev_flat.copy_(host_flat, non_blocking=True))
+    gbs = lambda ms: round(nbytes / (ms * 1e-3) / 1e9, 2)  # noqa: E731
+    return {
+        "blocks": n,
+        "bytes_per_direction": nbytes,
+        "block_bytes_k_plus_v": 2 * kc[0].numel() * kc.element_size(),
+        "swap_out_GBps": gbs(out_ms),
+        "swap_in_GBps": gbs(in_ms),
+        "contiguous_copy_d2h_GBps": gbs(d2h_ms),
+        "contiguous_copy_h2d_GBps": gbs(h2d_ms),
+        "swap_out_ms": round(out_ms, 3),
+        "swap_in_ms": round(in_ms, 3),
+    }
+
+
 def extra_row(w, P: int, fused: bool, r) -> dict:
     """One line of "extra_workloads": the same quantities as the headline, for another workload."""
     case = r["case"]
@@ -450,6 +504,7 @@ def main() -> int:
             rows.append(extra_row(we, we.partition_size, fused,
                                   run_workload(we, we.partition_size, fused, min(K, 100), args.warmup)))
         result["extra_workloads"] = rows
+        result["kv_swap"] = swap_row()
         result["graph_replay"] = [graph_row(wl.WORKLOADS[name], layers, min(K, 50), min(args.warmup, 5))
                                   for name, layers in GRAPH_WORKLOADS]
     print(json.dumps(result), flush=True)

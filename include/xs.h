@@ -265,6 +265,32 @@ int xs_paged_attn_reduce(const float* part_o, const float* part_m, const float* 
                          int partition_size, int max_partitions, int dtype, void* stream);
 
 /*
+ * KV block swap between the paged pools and a swap space in pinned host memory (the xserv
+ * README, xserv compare phase10...cf1e9e41: CPU swap-out / swap-in of the paged KV cache into
+ * pinned host memory, `--swap-space-gb`).
+ * The swap space is k_host, v_host: [num_slots, num_kv_heads, block_size, head_dim] in `dtype`,
+ * allocated pinned (hipHostMalloc, or torch pin_memory=True) by the caller; anything else is
+ * rejected with XS_EINVAL before any launch. One slot holds one pool block (all kv heads).
+ * xs_kv_swap_out: for i < num_pairs, slot dst_slots[i] becomes a bit copy of pool block
+ *   src_blocks[i] (K and V).
+ * xs_kv_swap_in:  for i < num_pairs, pool block dst_blocks[i] becomes a bit copy of slot
+ *   src_slots[i] (K and V).
+ * The index lists are int32 device arrays of num_pairs entries. A pair with an index outside
+ * [0, num_blocks) or [0, num_slots) is skipped. Two pairs must not share a destination (their
+ * order is not fixed). One launch moves the whole list; the GPU reads or writes the host memory
+ * directly over the host link. Asynchronous on `stream`, like the calls above: host memory is
+ * complete only once the stream has been synchronized.
+ */
+int xs_kv_swap_out(const void* k_cache, const void* v_cache, void* k_host, void* v_host,
+                   const int32_t* src_blocks, const int32_t* dst_slots, int num_pairs,
+                   int num_blocks, int num_slots, int num_kv_heads, int block_size, int head_dim,
+                   int dtype, void* stream);
+int xs_kv_swap_in(const void* k_host, const void* v_host, void* k_cache, void* v_cache,
+                  const int32_t* src_slots, const int32_t* dst_blocks, int num_pairs,
+                  int num_blocks, int num_slots, int num_kv_heads, int block_size, int head_dim,
+                  int dtype, void* stream);
+
+/*
  * Measurement aid, not part of the decode step: reads `bytes` (a multiple of 16) at `buf` with
  * 16-byte loads (nontemporal if `nontemporal` != 0) in a grid-stride loop, and writes at most
  * one word to `sink` (device memory, 4 bytes). Timing it gives the read rate that plain

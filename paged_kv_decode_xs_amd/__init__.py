@@ -12,6 +12,8 @@ from ._binding import (  # noqa: F401
     load_library,
     num_partitions,
     xs_kv_append,
+    xs_kv_swap_in,
+    xs_kv_swap_out,
     xs_last_error,
     xs_paged_attn_decode,
     xs_paged_attn_balanced_workspace_size,

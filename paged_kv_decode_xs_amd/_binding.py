@@ -63,6 +63,8 @@ SIGNATURES = {
                                    _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp],
     "xs_paged_attn_reduce_sinks": [_vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _vp],
     "xs_stream_read_probe": [_vp, ctypes.c_size_t, _vp, _i, _vp],
+    "xs_kv_swap_out": [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp],
+    "xs_kv_swap_in": [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp],
     "xs_step_graph_create": [ctypes.POINTER(XsStepDesc), _i, ctypes.POINTER(ctypes.c_void_p)],
     "xs_step_graph_launch": [_vp, _vp],
     "xs_step_graph_destroy": [_vp],
@@ -308,6 +310,38 @@ def xs_stream_read_probe(buf: torch.Tensor, sink: torch.Tensor, nontemporal: boo
     _need(sink.numel() * sink.element_size() >= 4, "sink must hold 4 bytes")
     _check("xs_stream_read_probe", load_library().xs_stream_read_probe(
         _ptr(buf), nbytes - nbytes % 16, _ptr(sink), int(bool(nontemporal)), _stream_handle(stream)))
+
+
+def _swap_checks(k_cache, v_cache, k_host, v_host, src, dst):
+    _dev(k_cache, v_cache, src, dst)
+    _need(v_cache.shape == k_cache.shape and k_cache.dim() == 4, "pools must be [NB, Hkv, BS, D] and alike")
+    for t in (k_host, v_host):
+        _need(not t.is_cuda and t.is_pinned() and t.is_contiguous(), "the swap space must be pinned, contiguous host tensors")
+    _need(k_host.shape[1:] == k_cache.shape[1:] and v_host.shape == k_host.shape,
+          "swap space must be [slots, Hkv, BS, D] like the pools")
+    _need(len({k_cache.dtype, v_cache.dtype, k_host.dtype, v_host.dtype}) == 1, "pool and swap-space dtypes differ")
+    _need(src.dtype == torch.int32 and dst.dtype == torch.int32 and src.dim() == 1 and src.shape == dst.shape,
+          "index lists must be int32 [num_pairs] device tensors of equal length")
+    NB, Hkv, BS, D = k_cache.shape
+    return NB, k_host.shape[0], Hkv, BS, D
+
+
+def xs_kv_swap_out(k_cache: torch.Tensor, v_cache: torch.Tensor, k_host: torch.Tensor, v_host: torch.Tensor,
+                   src_blocks: torch.Tensor, dst_slots: torch.Tensor, stream=None) -> None:
+    """Copy pool blocks src_blocks[i] into host slots dst_slots[i] (K and V), one launch."""
+    NB, S, Hkv, BS, D = _swap_checks(k_cache, v_cache, k_host, v_host, src_blocks, dst_slots)
+    _check("xs_kv_swap_out", load_library().xs_kv_swap_out(
+        _ptr(k_cache), _ptr(v_cache), _ptr(k_host), _ptr(v_host), _ptr(src_blocks), _ptr(dst_slots),
+        src_blocks.numel(), NB, S, Hkv, BS, D, _dtype_code(k_cache), _stream_handle(stream)))
+
+
+def xs_kv_swap_in(k_host: torch.Tensor, v_host: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                  src_slots: torch.Tensor, dst_blocks: torch.Tensor, stream=None) -> None:
+    """Copy host slots src_slots[i] into pool blocks dst_blocks[i] (K and V), one launch."""
+    NB, S, Hkv, BS, D = _swap_checks(k_cache, v_cache, k_host, v_host, src_slots, dst_blocks)
+    _check("xs_kv_swap_in", load_library().xs_kv_swap_in(
+        _ptr(k_host), _ptr(v_host), _ptr(k_cache), _ptr(v_cache), _ptr(src_slots), _ptr(dst_blocks),
+        src_slots.numel(), NB, S, Hkv, BS, D, _dtype_code(k_cache), _stream_handle(stream)))
 
 
 def xs_step_graph_create(descs) -> int:

@@ -432,3 +432,61 @@ XS_API int xs_step_graph_destroy(xs_step_graph* g) {
     return fail(XS_ELAUNCH, "xs_step_graph_destroy: %s", hipGetErrorString(e1 != hipSuccess ? e1 : e2));
   return ok();
 }
+
+// ------------------------------------------------------------------------------------------
+// KV block swap between the pools and pinned host memory.
+
+namespace {
+
+// The device address of pinned host memory at `p` (NULL if `p` is not pinned host memory).
+void* host_device_pointer(const void* p) {
+  void* d = nullptr;
+  if (hipHostGetDevicePointer(&d, const_cast<void*>(p), 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return d;
+}
+
+int swap_call(const char* who, bool out, const void* pool_k, const void* pool_v, const void* host_k,
+              const void* host_v, const int32_t* src_idx, const int32_t* dst_idx, int num_pairs, int num_blocks,
+              int num_slots, int num_kv_heads, int block_size, int head_dim, int dtype, void* stream) {
+  if (num_pairs < 0) return fail(XS_EINVAL, "%s: num_pairs = %d < 0", who, num_pairs);
+  if (num_blocks < 1 || num_slots < 1 || num_kv_heads < 1 || block_size < 1 || head_dim < 1)
+    return fail(XS_EINVAL, "%s: num_blocks, num_slots, num_kv_heads, block_size and head_dim must be >= 1", who);
+  if (dtype != XS_F32 && dtype != XS_BF16) return fail(XS_EUNSUPPORTED, "%s: dtype %d is not XS_F32 or XS_BF16", who, dtype);
+  const size_t block_bytes = (size_t)num_kv_heads * block_size * head_dim * elt_bytes(dtype);
+  if (block_bytes % 16 != 0) return fail(XS_EINVAL, "%s: a block (%zu bytes) is not a multiple of 16 bytes", who, block_bytes);
+  if (block_bytes / 16 > 0x7fffffffULL) return fail(XS_EINVAL, "%s: blocks too large", who);
+  if (num_pairs == 0) return ok();
+  if (!pool_k || !pool_v || !host_k || !host_v || !src_idx || !dst_idx)
+    return fail(XS_EINVAL, "%s: a required pointer is NULL", who);
+  if (!aligned16(pool_k) || !aligned16(pool_v) || !aligned16(host_k) || !aligned16(host_v))
+    return fail(XS_EINVAL, "%s: pools and host buffers must be 16-byte aligned", who);
+  void* dk = host_device_pointer(host_k);
+  void* dv = host_device_pointer(host_v);
+  if (!dk || !dv) return fail(XS_EINVAL, "%s: k_host and v_host must be pinned host memory (hipHostMalloc)", who);
+  (void)hipGetLastError();
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = out ? xs::launch_kv_swap(pool_k, pool_v, dk, dv, src_idx, dst_idx, num_pairs, num_blocks, num_slots,
+                                          block_bytes, s)
+                     : xs::launch_kv_swap(dk, dv, const_cast<void*>(pool_k), const_cast<void*>(pool_v), src_idx,
+                                          dst_idx, num_pairs, num_slots, num_blocks, block_bytes, s);
+  return launch_status(who, e);
+}
+
+}  // namespace
+
+XS_API int xs_kv_swap_out(const void* k_cache, const void* v_cache, void* k_host, void* v_host,
+                          const int32_t* src_blocks, const int32_t* dst_slots, int num_pairs, int num_blocks,
+                          int num_slots, int num_kv_heads, int block_size, int head_dim, int dtype, void* stream) {
+  return swap_call("xs_kv_swap_out", true, k_cache, v_cache, k_host, v_host, src_blocks, dst_slots, num_pairs,
+                   num_blocks, num_slots, num_kv_heads, block_size, head_dim, dtype, stream);
+}
+
+XS_API int xs_kv_swap_in(const void* k_host, const void* v_host, void* k_cache, void* v_cache,
+                         const int32_t* src_slots, const int32_t* dst_blocks, int num_pairs, int num_blocks,
+                         int num_slots, int num_kv_heads, int block_size, int head_dim, int dtype, void* stream) {
+  return swap_call("xs_kv_swap_in", false, k_cache, v_cache, k_host, v_host, src_slots, dst_blocks, num_pairs,
+                   num_blocks, num_slots, num_kv_heads, block_size, head_dim, dtype, stream);
+}

@@ -99,6 +99,13 @@ hipError_t launch_paged_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 // Heads handled together by one wavefront: the largest of 8, 4, 2, 1 that divides the group size.
 int heads_per_chunk(int group);
 
+// Block swap: pair i copies block src_idx[i] of (src_k, src_v) to block dst_idx[i] of (dst_k, dst_v),
+// block_bytes each (a multiple of 16); pairs with an index outside [0, n_src) / [0, n_dst) are skipped.
+// Host-side pointers must already be the device addresses of pinned host memory.
+hipError_t launch_kv_swap(const void* src_k, const void* src_v, void* dst_k, void* dst_v, const int32_t* src_idx,
+                          const int32_t* dst_idx, int num_pairs, int n_src, int n_dst, size_t block_bytes,
+                          hipStream_t stream);
+
 // Streaming-read probe over `bytes` (a multiple of 16) of device memory.
 hipError_t launch_stream_read(const void* buf, size_t bytes, unsigned* sink, bool nontemporal, hipStream_t stream);
 

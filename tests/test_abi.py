@@ -250,3 +250,30 @@ def test_step_graph_rejects_step_count_and_names_the_bad_step():
     arr[2].head_dim = 128
     arr[1].batch = 0
     assert lib.xs_step_graph_create(arr, 3, ctypes.byref(h)) == 1 and "step 1" in xb.xs_last_error()
+
+
+@pytest.mark.parametrize("fn", ["xs_kv_swap_out", "xs_kv_swap_in"])
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(n=-1), 1, "num_pairs"),
+    (dict(slots=0), 1, ">= 1"),
+    (dict(dt=9), 2, "dtype"),
+    (dict(d=3, bs=1, hkv=1, dt=B), 1, "multiple of 16"),
+    (dict(src=None), 1, "NULL"),
+    (dict(kh=FAKE + 8), 1, "aligned"),
+])
+def test_swap_rejects(fn, kw, status, needle):
+    a = dict(kc=FAKE, vc=FAKE, kh=FAKE, vh=FAKE, src=FAKE, dst=FAKE, n=4, nb=16, slots=8, hkv=2, bs=16, d=64, dt=B)
+    a.update(kw)
+    f = getattr(xb.load_library(), fn)
+    if fn == "xs_kv_swap_out":
+        st = f(a["kc"], a["vc"], a["kh"], a["vh"], a["src"], a["dst"], a["n"], a["nb"], a["slots"], a["hkv"], a["bs"],
+               a["d"], a["dt"], None)
+    else:
+        st = f(a["kh"], a["vh"], a["kc"], a["vc"], a["src"], a["dst"], a["n"], a["nb"], a["slots"], a["hkv"], a["bs"],
+               a["d"], a["dt"], None)
+    assert st == status
+    assert needle in xb.xs_last_error()
+
+
+def test_swap_empty_list_is_a_noop():
+    assert xb.load_library().xs_kv_swap_out(None, None, None, None, None, None, 0, 4, 4, 1, 16, 64, B, None) == 0
