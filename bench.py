@@ -342,6 +342,71 @@ def swap_row(reps: int = 10) -> dict:
     }
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_row(name: str = "qwen3_8b_prefill_c512", reps: int = 20) -> dict:
+    """Chunked prefill on the Qwen3-8B shape: the multi-token append and the causal attention of
+    the chunk, each timed alone (HIP events around single launches on the launch stream, median
+    of `reps`). The attention is a dense contraction on the matrix cores: its algorithmic flops
+    (4 * head_dim per (query head, chunk row, visible key)) over its time, against the bf16 dense
+    MFMA peak. The append moves bytes: read + write of every chunk row, against HBM peak."""
+    import torch
+
+    import paged_kv_decode_xs_amd as xs
+    from workloads.device import to_torch
+    from workloads.prefill import PREFILL_WORKLOADS, make_prefill_case
+
+    w = PREFILL_WORKLOADS[name]
+    case = make_prefill_case(w)
+    dt = w.dtype
+    q = to_torch(case.q, dt).cuda()
+    ks, vs = to_torch(case.k_src, dt).cuda(), to_torch(case.v_src, dt).cuda()
+    kc, vc = to_torch(case.k_cache, dt).cuda(), to_torch(case.v_cache, dt).cuda()
+    bt = torch.from_numpy(case.block_tables).cuda()
+    sp = torch.from_numpy(case.start_pos).cuda()
+    cl = torch.from_numpy(case.chunk_lens).cuda()
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def med(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    append_ms = med(lambda: xs.xs_kv_append_chunk(ks, vs, kc, vc, bt, sp, cl, stream=stream))
+    attn_ms = med(lambda: xs.xs_paged_attn_prefill(q, kc, vc, bt, sp, cl, w.scale, out=out, stream=stream))
+    finite = bool(torch.isfinite(out.float()).all().item())
+    flops = w.attention_flops()
+    tflops = flops / (attn_ms * 1e-3) / 1e12
+    ab = w.append_bytes()
+    gbs = ab / (append_ms * 1e-3) / 1e9
+    return {
+        "workload": w.name,
+        "description": w.description,
+        "chunk_rows": int(case.chunk_lens.sum()),
+        "attention_flops": flops,
+        "attention_us": round(attn_ms * 1e3, 2),
+        "attention_TFLOPs": round(tflops, 2),
+        "attention_frac_of_bf16_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "append_bytes": ab,
+        "append_us": round(append_ms * 1e3, 2),
+        "append_GBps": round(gbs, 2),
+        "append_frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "output_finite": finite,
+        "cache": "warm (the chunk's K/V fit in the Infinity Cache; the attention is compute-bound)",
+    }
+
+
 def extra_row(w, P: int, fused: bool, r) -> dict:
     """One line of "extra_workloads": the same quantities as the headline, for another workload."""
     case = r["case"]
@@ -505,6 +570,7 @@ def main() -> int:
                                   run_workload(we, we.partition_size, fused, min(K, 100), args.warmup)))
         result["extra_workloads"] = rows
         result["kv_swap"] = swap_row()
+        result["chunked_prefill"] = prefill_row()
         result["graph_replay"] = [graph_row(wl.WORKLOADS[name], layers, min(K, 50), min(args.warmup, 5))
                                   for name, layers in GRAPH_WORKLOADS]
     print(json.dumps(result), flush=True)

@@ -291,6 +291,53 @@ int xs_kv_swap_in(const void* k_host, const void* v_host, void* k_cache, void* v
                   int dtype, void* stream);
 
 /*
+ * Chunked prefill, step 1: multi-token paged append (xserv compare phase10...cf1e9e41,
+ * attention.rs, `reshape_and_cache_bf16` / `launch_reshape_and_cache_bf16`: a run of tokens of
+ * one sequence written from start_pos on through its block ids; here batched over sequences).
+ *
+ * For every sequence b with 0 <= start_pos[b], 0 <= n_b = chunk_lens[b] <= chunk_size and
+ * start_pos[b] + n_b <= max_blocks_per_seq * block_size, and every i < n_b: position
+ * p = start_pos[b] + i lies in block blk = block_tables[b, p / block_size] at slot
+ * p % block_size, and for every kv head g row k_cache[blk, g, p % block_size, :] becomes
+ * k_src[b, g, i, :] (v_cache likewise). A bit copy; nothing else in the pools changes. Rows
+ * i >= n_b of k_src/v_src are not read, sequences outside the conditions above are skipped, and
+ * so are positions whose block id is outside [0, num_blocks).
+ * Arguments: k_src, v_src [batch, num_kv_heads, chunk_size, head_dim] (read); k_cache, v_cache
+ * (written in place); block_tables [batch, max_blocks_per_seq], start_pos [batch], chunk_lens
+ * [batch] (int32, device, read). XS_BF16 or XS_F32. Two positions must not map the same slot.
+ * batch == 0 or chunk_size == 0 is a no-op.
+ */
+int xs_kv_append_chunk(const void* k_src, const void* v_src, void* k_cache, void* v_cache,
+                       const int32_t* block_tables, const int32_t* start_pos, const int32_t* chunk_lens,
+                       int batch, int num_kv_heads, int head_dim, int chunk_size, int block_size,
+                       int max_blocks_per_seq, int num_blocks, int dtype, void* stream);
+
+/*
+ * Chunked prefill, step 2: causal GQA attention of a chunk of queries over the paged pool
+ * (xserv compare phase10...cf1e9e41, attention.rs, `flash_attention(q, k, v, causal)`, GQA
+ * native, with its K/V read through the block table as the decode attention reads them).
+ *
+ * Row i < n_b = chunk_lens[b] of sequence b sits at position p = start_pos[b] + i and sees the
+ * keys at positions t = 0 .. p (the causal mask aligned to the end of the cached range; with
+ * start_pos = 0 it is the plain causal mask). With g = h / (num_q_heads / num_kv_heads):
+ *   s_t = scale * dot(q[b, h, i, :], K_t),  K_t = k_cache[block_tables[b, t / block_size], g,
+ *         t % block_size, :], V_t likewise,
+ *   out[b, h, i, :] = sum_{t <= p} exp(s_t - max s) V_t / sum_{t <= p} exp(s_t - max s).
+ * The chunk's own K/V must already be in the pool (xs_kv_append_chunk). Rows i >= n_b are
+ * written as zeros, and so are all rows of a sequence outside the conditions of
+ * xs_kv_append_chunk. Positions whose block id is outside [0, num_blocks) are skipped.
+ * Arguments: q, out [batch, num_q_heads, chunk_size, head_dim] bf16 (q read, out written);
+ * pools and index arrays as above (read). XS_BF16 only (XS_EUNSUPPORTED otherwise); products in
+ * fp32 from bf16 inputs, the probabilities rounded to bf16 for the P.V product, fp32 softmax
+ * statistics, out rounded to bf16. batch == 0 or chunk_size == 0 is a no-op.
+ */
+int xs_paged_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* start_pos, const int32_t* chunk_lens,
+                          float scale, void* out, int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                          int chunk_size, int block_size, int max_blocks_per_seq, int num_blocks, int dtype,
+                          void* stream);
+
+/*
  * Measurement aid, not part of the decode step: reads `bytes` (a multiple of 16) at `buf` with
  * 16-byte loads (nontemporal if `nontemporal` != 0) in a grid-stride loop, and writes at most
  * one word to `sink` (device memory, 4 bytes). Timing it gives the read rate that plain

@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     load_library,
     num_partitions,
     xs_kv_append,
+    xs_kv_append_chunk,
     xs_kv_swap_in,
     xs_kv_swap_out,
     xs_last_error,
@@ -20,6 +21,7 @@ from ._binding import (  # noqa: F401
     xs_paged_attn_decode_append,
     xs_paged_attn_decode_balanced,
     xs_paged_attn_decode_sinks,
+    xs_paged_attn_prefill,
     xs_paged_attn_reduce,
     xs_paged_attn_reduce_sinks,
     xs_step_graph_create,

@@ -68,6 +68,8 @@ SIGNATURES = {
     "xs_step_graph_create": [ctypes.POINTER(XsStepDesc), _i, ctypes.POINTER(ctypes.c_void_p)],
     "xs_step_graph_launch": [_vp, _vp],
     "xs_step_graph_destroy": [_vp],
+    "xs_kv_append_chunk": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp],
+    "xs_paged_attn_prefill": [_vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp],
     "xs_last_error": [],
     "xs_version": [],
 }
@@ -358,6 +360,49 @@ def xs_step_graph_launch(handle: int, stream=None) -> None:
 
 def xs_step_graph_destroy(handle: int) -> None:
     _check("xs_step_graph_destroy", load_library().xs_step_graph_destroy(handle))
+
+
+def _chunk_checks(B, block_tables, start_pos, chunk_lens):
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == B,
+          "block_tables must be int32 [batch, max_blocks_per_seq]")
+    _need(start_pos.dtype == torch.int32 and start_pos.shape == (B,), "start_pos must be int32 [batch]")
+    _need(chunk_lens.dtype == torch.int32 and chunk_lens.shape == (B,), "chunk_lens must be int32 [batch]")
+
+
+def xs_kv_append_chunk(k_src: torch.Tensor, v_src: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                       block_tables: torch.Tensor, start_pos: torch.Tensor, chunk_lens: torch.Tensor,
+                       stream=None) -> None:
+    """Write rows i < chunk_lens[b] of k_src/v_src [batch, Hkv, chunk, D] to positions start_pos[b] + i."""
+    _dev(k_src, v_src, k_cache, v_cache, block_tables, start_pos, chunk_lens)
+    NB, Hkv, BS, D = k_cache.shape
+    B, C = k_src.shape[0], k_src.shape[2]
+    _need(k_src.shape == (B, Hkv, C, D) and v_src.shape == k_src.shape, "k_src/v_src must be [batch, Hkv, chunk, D]")
+    _need(v_cache.shape == k_cache.shape, "k_cache and v_cache must have the same shape")
+    _need(len({k_src.dtype, v_src.dtype, k_cache.dtype, v_cache.dtype}) == 1, "K/V dtypes differ")
+    _chunk_checks(B, block_tables, start_pos, chunk_lens)
+    _check("xs_kv_append_chunk", load_library().xs_kv_append_chunk(
+        _ptr(k_src), _ptr(v_src), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(start_pos),
+        _ptr(chunk_lens), B, Hkv, D, C, BS, block_tables.shape[1], NB, _dtype_code(k_cache), _stream_handle(stream)))
+
+
+def xs_paged_attn_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                          start_pos: torch.Tensor, chunk_lens: torch.Tensor, scale: float,
+                          out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Causal attention of q [batch, Hq, chunk, D] (row i at position start_pos[b] + i) over the pools."""
+    _dev(q, k_cache, v_cache, block_tables, start_pos, chunk_lens, out)
+    B, Hq, C, D = q.shape
+    NB, Hkv, BS, D2 = k_cache.shape
+    _need(D2 == D and v_cache.shape == k_cache.shape, "pool shapes do not match q")
+    _need(q.dtype == k_cache.dtype == v_cache.dtype, "q and the pools must have the same dtype")
+    _chunk_checks(B, block_tables, start_pos, chunk_lens)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out)
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _check("xs_paged_attn_prefill", load_library().xs_paged_attn_prefill(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(start_pos), _ptr(chunk_lens), float(scale),
+        _ptr(out), B, Hq, Hkv, D, C, BS, block_tables.shape[1], NB, _dtype_code(q), _stream_handle(stream)))
+    return out
 
 
 def num_partitions(max_context_len: int, partition_size: int) -> int:

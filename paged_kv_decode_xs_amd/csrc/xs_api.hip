@@ -490,3 +490,74 @@ XS_API int xs_kv_swap_in(const void* k_host, const void* v_host, void* k_cache, 
   return swap_call("xs_kv_swap_in", false, k_cache, v_cache, k_host, v_host, src_slots, dst_blocks, num_pairs,
                    num_blocks, num_slots, num_kv_heads, block_size, head_dim, dtype, stream);
 }
+
+// ------------------------------------------------------------------------------------------
+// Chunked prefill: multi-token append and causal attention of the chunk.
+
+XS_API int xs_kv_append_chunk(const void* k_src, const void* v_src, void* k_cache, void* v_cache,
+                              const int32_t* block_tables, const int32_t* start_pos, const int32_t* chunk_lens,
+                              int batch, int num_kv_heads, int head_dim, int chunk_size, int block_size,
+                              int max_blocks_per_seq, int num_blocks, int dtype, void* stream) {
+  const char* who = "xs_kv_append_chunk";
+  int st = check_pool_args(who, batch, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, dtype);
+  if (st != XS_OK) return st;
+  if (chunk_size < 0) return fail(XS_EINVAL, "%s: chunk_size = %d < 0", who, chunk_size);
+  if (batch == 0 || chunk_size == 0) return ok();
+  if (!k_src || !v_src || !k_cache || !v_cache || !block_tables || !start_pos || !chunk_lens)
+    return fail(XS_EINVAL, "%s: a required pointer is NULL", who);
+  if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(XS_EINVAL, "%s: k_src, v_src, k_cache and v_cache must be 16-byte aligned", who);
+  if (2LL * batch * num_kv_heads * chunk_size * (head_dim * elt_bytes(dtype) / 16) > 0x7fffffffLL * 256LL)
+    return fail(XS_EINVAL, "%s: batch * num_kv_heads * chunk_size too large", who);
+  (void)hipGetLastError();
+  return launch_status(who, xs::launch_kv_append_chunk(k_src, v_src, k_cache, v_cache, block_tables, start_pos,
+                                                       chunk_lens, batch, num_kv_heads, head_dim, chunk_size,
+                                                       block_size, max_blocks_per_seq, num_blocks, elt_bytes(dtype),
+                                                       static_cast<hipStream_t>(stream)));
+}
+
+XS_API int xs_paged_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* start_pos, const int32_t* chunk_lens,
+                                 float scale, void* out, int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                 int chunk_size, int block_size, int max_blocks_per_seq, int num_blocks, int dtype,
+                                 void* stream) {
+  const char* who = "xs_paged_attn_prefill";
+  int st = check_pool_args(who, batch, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, dtype);
+  if (st != XS_OK) return st;
+  if (dtype != XS_BF16) return fail(XS_EUNSUPPORTED, "%s: only XS_BF16 is implemented", who);
+  if (num_q_heads < 1) return fail(XS_EINVAL, "%s: num_q_heads = %d < 1", who, num_q_heads);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(XS_EINVAL, "%s: num_q_heads = %d is not a multiple of num_kv_heads = %d", who, num_q_heads,
+                num_kv_heads);
+  if (chunk_size < 0) return fail(XS_EINVAL, "%s: chunk_size = %d < 0", who, chunk_size);
+  if (!isfinite(scale)) return fail(XS_EINVAL, "%s: scale is not finite", who);
+  const int group = num_q_heads / num_kv_heads;
+  if ((long long)chunk_size * group > 0x7fffffffLL - 64)
+    return fail(XS_EINVAL, "%s: chunk_size * (num_q_heads / num_kv_heads) too large", who);
+  if (batch == 0 || chunk_size == 0) return ok();
+  const long long grid = (long long)batch * num_kv_heads * xs::prefill_row_blocks(chunk_size, group);
+  if (grid > 0x7fffffffLL) return fail(XS_EINVAL, "%s: %lld workgroups exceed the launch limit", who, grid);
+  if (!q || !k_cache || !v_cache || !block_tables || !start_pos || !chunk_lens || !out)
+    return fail(XS_EINVAL, "%s: a required pointer is NULL", who);
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return fail(XS_EINVAL, "%s: q, k_cache, v_cache and out must be 16-byte aligned", who);
+  xs::PrefillArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.start_pos = start_pos;
+  a.chunk_lens = chunk_lens;
+  a.scale = scale;
+  a.out = out;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.chunk = chunk_size;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  (void)hipGetLastError();
+  return launch_status(who, xs::launch_paged_prefill(a, static_cast<hipStream_t>(stream)));
+}

@@ -106,6 +106,29 @@ hipError_t launch_kv_swap(const void* src_k, const void* src_v, void* dst_k, voi
                           const int32_t* dst_idx, int num_pairs, int n_src, int n_dst, size_t block_bytes,
                           hipStream_t stream);
 
+// Chunked prefill (xs_prefill.hip). The append copies rows i < chunk_lens[b] of k_src/v_src
+// [batch, num_kv_heads, chunk, head_dim] to positions start_pos[b] + i.
+hipError_t launch_kv_append_chunk(const void* k_src, const void* v_src, void* k_cache, void* v_cache,
+                                  const int32_t* block_tables, const int32_t* start_pos, const int32_t* chunk_lens,
+                                  int batch, int num_kv_heads, int head_dim, int chunk, int block_size,
+                                  int max_blocks_per_seq, int num_blocks, int elt_bytes, hipStream_t stream);
+
+// Causal attention of a chunk of bf16 queries [batch, num_q_heads, chunk, head_dim] over the pool.
+struct PrefillArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* start_pos;
+  const int32_t* chunk_lens;
+  float scale;
+  void* out;
+  int batch, num_q_heads, num_kv_heads, head_dim, chunk, block_size, max_blocks_per_seq, num_blocks;
+};
+// Workgroups per (sequence, kv head) of the prefill attention: chunk * group rows, 64 per group.
+int prefill_row_blocks(int chunk, int group);
+hipError_t launch_paged_prefill(const PrefillArgs& a, hipStream_t stream);
+
 // Streaming-read probe over `bytes` (a multiple of 16) of device memory.
 hipError_t launch_stream_read(const void* buf, size_t bytes, unsigned* sink, bool nontemporal, hipStream_t stream);
 

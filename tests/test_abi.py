@@ -277,3 +277,67 @@ def test_swap_rejects(fn, kw, status, needle):
 
 def test_swap_empty_list_is_a_noop():
     assert xb.load_library().xs_kv_swap_out(None, None, None, None, None, None, 0, 4, 4, 1, 16, 64, B, None) == 0
+
+
+def _append_chunk(**kw):
+    a = dict(ks=FAKE, vs=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sp=FAKE, cl=FAKE, batch=2, hkv=2, d=128, c=16, bs=16,
+             mbps=4, nb=16, dt=B)
+    a.update(kw)
+    return xb.load_library().xs_kv_append_chunk(a["ks"], a["vs"], a["kc"], a["vc"], a["bt"], a["sp"], a["cl"],
+                                                 a["batch"], a["hkv"], a["d"], a["c"], a["bs"], a["mbps"], a["nb"],
+                                                 a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(batch=-1), 1, "batch"),
+    (dict(c=-2), 1, "chunk_size"),
+    (dict(d=96), 2, "head_dim"),
+    (dict(bs=12), 2, "block_size"),
+    (dict(dt=7), 2, "dtype"),
+    (dict(sp=None), 1, "NULL"),
+    (dict(cl=None), 1, "NULL"),
+    (dict(ks=FAKE + 4), 1, "aligned"),
+    (dict(nb=0), 1, "num_blocks"),
+])
+def test_append_chunk_rejects(kw, status, needle):
+    assert _append_chunk(**kw) == status
+    assert needle in xb.xs_last_error()
+
+
+def test_append_chunk_empty_is_a_noop():
+    assert _append_chunk(batch=0, ks=None, vs=None) == 0
+    assert _append_chunk(c=0, ks=None, vs=None, sp=None) == 0
+
+
+def _prefill(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sp=FAKE, cl=FAKE, scale=0.125, out=FAKE, batch=2, hq=8, hkv=2, d=128,
+             c=16, bs=16, mbps=4, nb=16, dt=B)
+    a.update(kw)
+    return xb.load_library().xs_paged_attn_prefill(a["q"], a["kc"], a["vc"], a["bt"], a["sp"], a["cl"], a["scale"],
+                                                    a["out"], a["batch"], a["hq"], a["hkv"], a["d"], a["c"], a["bs"],
+                                                    a["mbps"], a["nb"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dt=F), 2, "XS_BF16"),
+    (dict(d=80), 2, "head_dim"),
+    (dict(bs=64), 2, "block_size"),
+    (dict(hq=6, hkv=4), 1, "multiple"),
+    (dict(hq=0), 1, "num_q_heads"),
+    (dict(c=-1), 1, "chunk_size"),
+    (dict(scale=float("nan")), 1, "scale"),
+    (dict(out=None), 1, "NULL"),
+    (dict(bt=None), 1, "NULL"),
+    (dict(q=FAKE + 2), 1, "aligned"),
+    (dict(out=FAKE + 8), 1, "aligned"),
+    (dict(c=1 << 30, hq=8, hkv=1), 1, "too large"),
+    (dict(batch=1 << 20, hkv=64, hq=64, c=1 << 16), 1, "launch limit"),
+])
+def test_prefill_rejects(kw, status, needle):
+    assert _prefill(**kw) == status
+    assert needle in xb.xs_last_error()
+
+
+def test_prefill_empty_is_a_noop():
+    assert _prefill(batch=0, q=None, out=None) == 0
+    assert _prefill(c=0, q=None, out=None) == 0

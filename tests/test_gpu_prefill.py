@@ -1,0 +1,173 @@
+"""Chunked prefill (xs_kv_append_chunk + xs_paged_attn_prefill) against the prefill oracle (needs an
+MI355X).
+
+The append must reproduce the oracle's pools bit for bit (only the chunk's slots change, the NaN
+poison elsewhere stays). The attention output is compared element by element with the fp64
+oracle at the bf16 bar (2e-2 absolute + 2e-2 relative); rows past chunk_lens[b] must be exactly
+zero. Shapes span several 64-row workgroups and 32-token key tiles with ragged tails, GQA groups
+that do and do not divide 16 (1, 3, 4, 6, 8, 12), head_dim 64/128, block_size 8/16/32, chunks
+that start at 0 or deep into a cached prefix, empty chunks and sequences outside the valid range.
+The Qwen3-8B 512-token chunk workload (the timed one) is checked in full for the append and on
+sampled rows for the attention: a run of rows [a, a+k) of the chunk is what the oracle gives for
+a chunk that starts at start_pos + a (the chunking invariance pinned on the CPU).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_decode_xs_amd as xs
+from tests.gpu_common import TOL, as_f64, assert_close, log
+from workloads.device import to_numpy_bits, to_torch
+from workloads.prefill import PREFILL_WORKLOADS, PrefillWorkload, make_prefill_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _library():
+    xs.load_library()
+    torch.cuda.init()
+    yield
+
+
+def _to_dev(case):
+    dt = case.workload.dtype
+    return {
+        "q": to_torch(case.q, dt).cuda(),
+        "k_src": to_torch(case.k_src, dt).cuda(),
+        "v_src": to_torch(case.v_src, dt).cuda(),
+        "k_cache": to_torch(case.k_cache, dt).cuda(),
+        "v_cache": to_torch(case.v_cache, dt).cuda(),
+        "bt": torch.from_numpy(case.block_tables).cuda(),
+        "sp": torch.from_numpy(case.start_pos).cuda(),
+        "cl": torch.from_numpy(case.chunk_lens).cuda(),
+    }
+
+
+def _run(dev, scale):
+    xs.xs_kv_append_chunk(dev["k_src"], dev["v_src"], dev["k_cache"], dev["v_cache"], dev["bt"], dev["sp"], dev["cl"])
+    out = xs.xs_paged_attn_prefill(dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"], dev["sp"], dev["cl"], scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check_pools(dev, kp, vp):
+    for name, exp in (("k_cache", kp), ("v_cache", vp)):
+        got = to_numpy_bits(dev[name])
+        assert np.array_equal(got.view(np.uint8), exp.view(np.uint8)), f"{name} differs after the chunk append"
+
+
+def _full_check(w, label):
+    log(f"[gpu] prefill {label}: Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim} BS={w.block_size} "
+        f"C={w.chunk} start={w.start_pos} n={w.chunk_lens}")
+    case = make_prefill_case(w)
+    kp, vp = oracle.kv_append_chunk(case.k_cache, case.v_cache, case.k_src, case.v_src, case.block_tables,
+                                    case.start_pos, case.chunk_lens, w.block_size)
+    exp = oracle.paged_prefill_attention(case.q, kp, vp, case.block_tables, case.start_pos, case.chunk_lens, w.scale,
+                                         w.block_size, "bf16")
+    dev = _to_dev(case)
+    out = _run(dev, w.scale)
+    _check_pools(dev, kp, vp)
+    got = as_f64(out)
+    atol, rtol = TOL["bf16"]
+    err = assert_close(got, exp, atol, rtol, f"prefill {label}")
+    for b, n in enumerate(case.chunk_lens.tolist()):
+        assert not got[b, :, n:].any(), f"rows past chunk_lens[{b}] = {n} are not zero"
+    # Deterministic: a second run on the same inputs gives the same bits.
+    out2 = xs.xs_paged_attn_prefill(dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"], dev["sp"], dev["cl"], w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    return err
+
+
+SHAPES = [
+    # Hq, Hkv, D, BS, C, start_pos, chunk_lens
+    (8, 2, 64, 16, 24, (0, 37, 5), (24, 11, 1)),
+    (6, 2, 128, 8, 21, (3, 64), (21, 20)),
+    (12, 1, 64, 32, 9, (40, 0), (9, 0)),
+    (2, 2, 64, 16, 40, (0, 60), (40, 33)),
+    (32, 8, 128, 16, 70, (0, 130, 257), (70, 64, 3)),
+    (64, 8, 64, 16, 33, (100, 0), (33, 17)),
+    (12, 2, 128, 32, 50, (31, 200, 0, 77), (50, 49, 50, 1)),
+    (16, 16, 128, 16, 130, (0,), (130,)),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"Hq{s[0]}_Hkv{s[1]}_D{s[2]}_BS{s[3]}_C{s[4]}")
+def test_prefill_matches_oracle(shape):
+    Hq, Hkv, D, BS, C, sp, cl = shape
+    mbps = -(-max(s + n for s, n in zip(sp, cl)) // BS) + 2
+    w = PrefillWorkload(name="t", description="", dtype="bf16", num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                        block_size=BS, chunk=C, start_pos=sp, chunk_lens=cl, max_blocks_per_seq=mbps,
+                        seed=hash(shape) % 1000)
+    _full_check(w, f"Hq{Hq} Hkv{Hkv} D{D} BS{BS} C{C}")
+
+
+def test_invalid_sequences_get_zero_rows_and_no_append():
+    w = PrefillWorkload(name="t", description="", dtype="bf16", num_q_heads=8, num_kv_heads=2, head_dim=64,
+                        block_size=16, chunk=20, start_pos=(0, 10, 5, 16), chunk_lens=(20, 20, 7, 12),
+                        max_blocks_per_seq=3, seed=11)
+    log("[gpu] prefill invalid ranges")
+    case = make_prefill_case(w)
+    dev = _to_dev(case)
+    # Sequence 1: start_pos < 0. Sequence 2: chunk_lens > chunk. Sequence 3: start + n > 48 slots.
+    sp = torch.tensor([0, -1, 5, 40], dtype=torch.int32)
+    cl = torch.tensor([20, 20, 21, 12], dtype=torch.int32)
+    dev["sp"].copy_(sp)
+    dev["cl"].copy_(cl)
+    out = _run(dev, w.scale)
+    valid = np.array([True, False, False, False])
+    kp, vp = oracle.kv_append_chunk(case.k_cache, case.v_cache, case.k_src[valid], case.v_src[valid],
+                                    case.block_tables[valid], case.start_pos[valid], case.chunk_lens[valid],
+                                    w.block_size)
+    _check_pools(dev, kp, vp)
+    exp = oracle.paged_prefill_attention(case.q[:1], kp, vp, case.block_tables[:1], case.start_pos[:1],
+                                         case.chunk_lens[:1], w.scale, w.block_size, "bf16")
+    got = as_f64(out)
+    assert_close(got[:1], exp, *TOL["bf16"], "prefill valid sequence")
+    assert not got[1:].any()
+
+
+def test_append_chunk_f32_bit_exact():
+    rng = np.random.default_rng(12)
+    NB, Hkv, BS, D, C = 40, 3, 8, 64, 17
+    log("[gpu] append chunk f32")
+    k = rng.standard_normal((NB, Hkv, BS, D)).astype(np.float32)
+    v = rng.standard_normal((NB, Hkv, BS, D)).astype(np.float32)
+    ks = rng.standard_normal((3, Hkv, C, D)).astype(np.float32)
+    vs = rng.standard_normal((3, Hkv, C, D)).astype(np.float32)
+    bt = rng.permutation(NB)[:3 * 8].reshape(3, 8).astype(np.int32)
+    sp = np.array([0, 9, 40], np.int32)
+    cl = np.array([17, 5, 0], np.int32)
+    kc, vc = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+    xs.xs_kv_append_chunk(torch.from_numpy(ks).cuda(), torch.from_numpy(vs).cuda(), kc, vc, torch.from_numpy(bt).cuda(),
+                          torch.from_numpy(sp).cuda(), torch.from_numpy(cl).cuda())
+    torch.cuda.synchronize()
+    ek, ev = oracle.kv_append_chunk(k, v, ks, vs, bt, sp, cl, BS)
+    assert np.array_equal(kc.cpu().numpy().view(np.uint32), ek.view(np.uint32))
+    assert np.array_equal(vc.cpu().numpy().view(np.uint32), ev.view(np.uint32))
+
+
+def test_qwen3_prefill_workload_sampled_rows():
+    w = PREFILL_WORKLOADS["qwen3_8b_prefill_c512"]
+    log(f"[gpu] prefill {w.name} (full size, sampled rows)")
+    case = make_prefill_case(w)
+    kp, vp = oracle.kv_append_chunk(case.k_cache, case.v_cache, case.k_src, case.v_src, case.block_tables,
+                                    case.start_pos, case.chunk_lens, w.block_size)
+    dev = _to_dev(case)
+    out = _run(dev, w.scale)
+    _check_pools(dev, kp, vp)
+    got = as_f64(out)
+    assert np.isfinite(got).all()
+    atol, rtol = TOL["bf16"]
+    rng = np.random.default_rng(13)
+    for b in range(w.batch):
+        n = int(case.chunk_lens[b])
+        for a in sorted({0, n - 3, *rng.integers(0, n - 3, 2).tolist()}):
+            k = 3
+            exp = oracle.paged_prefill_attention(case.q[b:b + 1, :, a:a + k], kp, vp, case.block_tables[b:b + 1],
+                                                 case.start_pos[b:b + 1] + a, np.array([k], np.int32), w.scale,
+                                                 w.block_size, "bf16")
+            assert_close(got[b:b + 1, :, a:a + k], exp[:, :, :k], atol, rtol, f"{w.name} b={b} rows {a}..{a + k - 1}")

@@ -69,3 +69,55 @@ def test_rmsnorm_rows():
     # All rows share one gain vector, so the per-column RMS over rows deviates coherently.
     col = np.sqrt((q.reshape(-1, q.shape[-1]) ** 2).mean(0))
     assert col.std() > 0.03
+
+
+# Chunked-prefill inputs.
+from workloads.prefill import PREFILL_WORKLOADS, PrefillWorkload, make_prefill_case  # noqa: E402
+
+
+def _tiny_prefill(**kw):
+    a = dict(name="t", description="", dtype="bf16", num_q_heads=4, num_kv_heads=2, head_dim=64, block_size=16,
+             chunk=20, start_pos=(0, 13, 40), chunk_lens=(20, 7, 0), max_blocks_per_seq=5, seed=1)
+    a.update(kw)
+    return PrefillWorkload(**a)
+
+
+def test_prefill_case_is_seeded_and_poisons_uncached_slots():
+    w = _tiny_prefill()
+    a, b = make_prefill_case(w), make_prefill_case(w)
+    for f in ("q", "k_src", "v_src", "k_cache", "v_cache", "block_tables"):
+        assert np.array_equal(getattr(a, f), getattr(b, f))
+    BS = w.block_size
+    for s in range(w.batch):
+        s0, n = int(a.start_pos[s]), int(a.chunk_lens[s])
+        nblk = -(-(s0 + n) // BS)
+        for p in range(nblk * BS):
+            blk = int(a.block_tables[s, p // BS])
+            row = a.k_cache[blk, :, p % BS, :]
+            assert (row == 0x7FC0).all() == (p >= s0), (s, p)
+        assert (a.block_tables[s, nblk:] == -1).all()
+    used = set(a.block_tables[a.block_tables >= 0].tolist())
+    assert len(used) == int(sum(-(-(s0 + n) // BS) for s0, n in zip(w.start_pos, w.chunk_lens)))
+    for blk in set(range(a.k_cache.shape[0])) - used:
+        assert (a.k_cache[blk] == 0x7FC0).all()
+
+
+def test_prefill_key_visits_and_flops():
+    w = _tiny_prefill()
+    brute = sum(s0 + i + 1 for s0, n in zip(w.start_pos, w.chunk_lens) for i in range(n))
+    assert w.key_visits() == brute
+    assert w.attention_flops() == 4 * 64 * 4 * brute
+    assert w.append_bytes() == 2 * 2 * 27 * 2 * 64 * 2
+
+
+def test_prefill_workloads_are_valid():
+    for w in PREFILL_WORKLOADS.values():
+        assert w.batch == len(w.chunk_lens)
+        assert max(s + n for s, n in zip(w.start_pos, w.chunk_lens)) <= w.max_blocks_per_seq * w.block_size
+
+
+def test_prefill_case_rejects_bad_ranges():
+    with pytest.raises(ValueError):
+        make_prefill_case(_tiny_prefill(chunk_lens=(21, 7, 0)))
+    with pytest.raises(ValueError):
+        make_prefill_case(_tiny_prefill(start_pos=(0, 13, 90)))
