@@ -40,6 +40,14 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source additions. The prefill attention keeps its MFMA accumulators in VGPRs (it rescales
+# them with vector ALU ops); the default heuristic puts them in AGPRs and copies them around
+# every matrix op.
+FILE_FLAGS = {
+    "xs_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def hipcc() -> str:
     env = os.environ.get("HIPCC")
     if env:
@@ -69,7 +77,8 @@ def build(verbose: bool = False, jobs: Optional[int] = None) -> str:
     cc = hipcc()
     srcs = sources()
     objs = [os.path.join(BUILD_DIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
-    cmds = [[cc, *COMMON_FLAGS, "-c", s, "-o", o] for s, o in zip(srcs, objs)]
+    cmds = [[cc, *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(s), []), "-c", s, "-o", o]
+            for s, o in zip(srcs, objs)]
     jobs = jobs or min(len(cmds), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         for cmd, fut in [(c, ex.submit(_run, c)) for c in cmds]:

@@ -7,22 +7,22 @@
 // attention with native GQA. Here a chunk row i of sequence b sits at position p = start_pos[b] + i
 // and sees the keys at positions 0..p (the causal mask aligned to the end of the cached range).
 //
-// Attention kernel. A workgroup of four wavefronts owns 64 consecutive "rows" of one
+// Attention kernel. A workgroup of four wavefronts owns 128 consecutive "rows" of one
 // (sequence, kv head): row rho = i * G + r is chunk position i of query head g * G + r (G query
 // heads per kv head), so one K/V tile in LDS serves every head of the group. Each wavefront
-// owns 16 rows (one per lane column) and walks the 32-token key tiles up to its last row's
-// position:
-//   scores  S^T[32 tokens x 16 rows] as two v_mfma_f32_16x16x32_bf16, half h taking the tokens
-//           2m + h (m = 0..15). Lane l then holds the scores of tokens 8(l/16) .. 8(l/16)+7 of
-//           row l%16: the row max and sum are a reduction over the lane's 8 values and the
-//           four lanes l%16 + 16j. The accumulator rescale is per lane.
-//   P.V     O^T[D x 16 rows] += V^T[D x 32] . P^T[32 x 16] with v_mfma_f32_16x16x32_bf16, D/16
-//           of them. The B operand (P^T, rounded to bf16) is exactly what the score MFMAs left
-//           in each lane. The A operand needs 8 tokens of one d per lane, so V is staged in
-//           LDS transposed ([d][token], 64 bytes per d row, 16-byte slots XOR-swizzled by d)
-//           and read back 16 bytes at a time.
-// The next tile is loaded into registers while the current one is processed (double-buffered
-// LDS, one barrier per tile). Tokens past the causal limit of a row get score -inf; tiles past
+// owns 32 rows (one per lane column n = lane % 32) and walks the 32-token key tiles up to its
+// last row's position:
+//   scores  S^T[32 tokens x 32 rows] = K . Q^T with v_mfma_f32_32x32x16_bf16 (D/16 of them, q in
+//           registers). Lane l then holds 16 scores of row l%32 (tokens 8(r/4) + 4(l/32) + r%4):
+//           the row max and sum are a reduction over the lane's 16 values and one lane swap;
+//           the accumulator rescale is per lane.
+//   P.V     O^T[D x 32 rows] += V^T[D x 16] . P^T[16 x 32] with v_mfma_f32_32x32x16_bf16, two
+//           token halves per 32-wide d block. The B operand (P^T, rounded to bf16) is exactly
+//           what the score MFMAs left in each lane. The A operand needs 8 tokens of one d per
+//           lane, so V is staged in LDS transposed ([d][token], 64 bytes per d row, 16-byte
+//           slots XOR-swizzled by d) and read back 16 bytes at a time.
+// The next two tiles are loaded into registers while the current one is processed
+// (double-buffered LDS, one barrier per tile). Tokens past the causal limit of a row get score -inf; tiles past
 // the workgroup's last position are never loaded, and K/V of positions past it are zero.
 #include <math.h>
 
@@ -81,10 +81,13 @@ struct PrefillParams {
   int batch, num_q_heads, num_kv_heads, group, chunk, row_blocks, bs_log2, max_blocks_per_seq, num_blocks;
 };
 
+typedef float __attribute__((ext_vector_type(16))) float16_t;
+
 constexpr int kTileTokens = 32;
-constexpr int kRowsPerWave = 16;
+constexpr int kRowsPerWave = 32;
 constexpr int kWaves = 4;
 constexpr int kRowsPerGroup = kRowsPerWave * kWaves;
+constexpr float kRescaleLog2 = 8.f;  // weights stay below 2^8 between rescales
 
 template <int D>
 struct PrefillLds {
@@ -97,11 +100,15 @@ struct PrefillLds {
   static constexpr int LOADS = kTileTokens * ND / (64 * kWaves);  // 16-byte pieces per thread per tile
 };
 
-// LDS row of token t in the K tile: score half h = t % 2 reads rows 16h .. 16h+15 in order.
-__device__ __forceinline__ int k_row(int t) { return 16 * (t & 1) + (t >> 1); }
-// Column of token t in a V^T row: lane group j's 16-byte slot j holds tokens 8j .. 8j+7 in the
-// order of its score registers (element 4h + i is token 8j + 2i + h).
-__device__ __forceinline__ int vt_col(int t) { return 8 * (t >> 3) + 4 * (t & 1) + ((t & 7) >> 1); }
+__device__ __forceinline__ uint4 mask4(const uint4 v, uint32_t m) {
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
+// Score register r of lane half hl holds token 8(r/4) + 4hl + r%4 of the tile.
+__device__ __forceinline__ int score_token(int r, int hl) { return 8 * (r >> 2) + 4 * hl + (r & 3); }
+// Column of token t in a V^T row. The 16-byte slot 2u + hl holds, in element order e = 0..7, the
+// tokens of score registers 8u .. 8u+7 of lane half hl: the B operand of P.V step u.
+__device__ __forceinline__ int vt_col(int t) { return 8 * (2 * (t >> 4) + ((t >> 2) & 1)) + 4 * ((t >> 3) & 1) + (t & 3); }
 // Slot swizzle of V^T row d: conflict-free 16-byte reads of 8 consecutive d rows.
 __device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 3)) & 3; }
 
@@ -109,13 +116,14 @@ template <int D>
 __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillParams prm) {
   using LD = PrefillLds<D>;
   constexpr int ND = LD::ND;
-  constexpr int KK = D / 32;
-  constexpr int MD = D / 16;
+  constexpr int KS = D / 16;  // score steps (16 d each)
+  constexpr int MD = D / 32;  // 32-wide d blocks of the output
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * LD::BUF_BYTES];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int j = lane >> 4, c = lane & 15;
+  const int n = lane & 31, hl = lane >> 5;  // score column (row of the chunk) and lane half
+  const int j = lane >> 4, c = lane & 15;   // loader coordinates
 
   // Workgroup -> (row block, sequence, kv head); the last row blocks (most keys) go first, and
   // the workgroups of one (sequence, kv head) share blockIdx.x mod 8 (one XCD's L2) when the
@@ -129,36 +137,36 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillParams prm) {
   const int C = prm.chunk;
   const int BS = 1 << prm.bs_log2;
 
-  int s0 = prm.start_pos[b], n = prm.chunk_lens[b];
-  if (s0 < 0 || n < 0 || n > C || (long long)s0 + n > (long long)prm.max_blocks_per_seq * BS) {
+  int s0 = prm.start_pos[b], nlen = prm.chunk_lens[b];
+  if (s0 < 0 || nlen < 0 || nlen > C || (long long)s0 + nlen > (long long)prm.max_blocks_per_seq * BS) {
     s0 = 0;
-    n = 0;  // a sequence with an invalid range gets zero rows
+    nlen = 0;  // a sequence with an invalid range gets zero rows
   }
   const int rows_total = C * G;
   const int rho0_wg = rb * kRowsPerGroup;
   const int rho0 = rho0_wg + wave * kRowsPerWave;
 
-  // This lane's row (column of the score tile).
-  const int rho = rho0 + c;
+  // This lane's row (column n of the score tile).
+  const int rho = rho0 + n;
   const int i_c = rho / G;
   const int h_c = g * G + rho % G;
   const bool row_exists = rho < rows_total;
-  const bool row_valid = row_exists && i_c < n;
+  const bool row_valid = row_exists && i_c < nlen;
   const int pos_c = s0 + i_c;  // last key position of this row
   const size_t out_row = ((size_t)b * prm.num_q_heads + h_c) * C + i_c;
 
   // Last valid chunk position of the workgroup and of this wavefront.
-  const int i_hi_wg = min((min(rho0_wg + kRowsPerGroup, rows_total) - 1) / G, n - 1);
+  const int i_hi_wg = min((min(rho0_wg + kRowsPerGroup, rows_total) - 1) / G, nlen - 1);
   const int i_lo_wave = rho0 / G;
-  const int i_hi_wave = min((min(rho0 + kRowsPerWave, rows_total) - 1) / G, n - 1);
-  const bool wave_active = rho0 < rows_total && i_lo_wave < n;
+  const int i_hi_wave = min((min(rho0 + kRowsPerWave, rows_total) - 1) / G, nlen - 1);
+  const bool wave_active = rho0 < rows_total && i_lo_wave < nlen;
   const int ntiles = i_hi_wg >= rho0_wg / G ? (s0 + i_hi_wg) / kTileTokens + 1 : 0;
   const int wave_tiles = wave_active ? (s0 + i_hi_wave) / kTileTokens + 1 : 0;
   const int kmax = s0 + i_hi_wg;  // last key position any row of the workgroup reads
 
-  float4_t acc[MD];
+  float16_t acc[MD];
 #pragma unroll
-  for (int md = 0; md < MD; ++md) acc[md] = float4_t{0.f, 0.f, 0.f, 0.f};
+  for (int md = 0; md < MD; ++md) acc[md] = float16_t{};
   float m_run = -INFINITY, l_part = 0.f;
 
   if (ntiles > 0) {
@@ -166,43 +174,75 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillParams prm) {
     const int Hkv = prm.num_kv_heads;
     auto block_ok = [&](int blk) { return blk >= 0 && blk < prm.num_blocks; };
 
-    // B operand of the scores: q[row][32kk + 8j .. +8].
-    uint4 qop[KK];
+    // B operand of the scores: q[row][16ks + 8hl .. +8] (rows outside the chunk read row 0 and
+    // become zeros; selects are per word, so nothing goes through private memory).
+    // A negative scale is taken as |scale| with q negated (a sign-bit flip, exact), so scores
+    // are always scaled by a positive factor and their max can be taken before scaling.
+    const uint32_t qmask = row_valid ? 0xffffffffu : 0u;
+    const uint32_t qsign = prm.scale_log2e < 0.f ? 0x80008000u : 0u;
+    // At least FLT_MIN, so a masked -inf score stays -inf (scale 0 gives uniform weights).
+    const float sl2 = fmaxf(fabsf(prm.scale_log2e), 1.17549435e-38f);
+    const size_t q_row = row_valid ? out_row : 0;
+    uint4 qop[KS];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      qop[kk] = row_valid ? prm.q[out_row * ND + 4 * kk + j] : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 qv = mask4(prm.q[q_row * ND + 2 * ks + hl], qmask);
+      qop[ks] = make_uint4(qv.x ^ (qsign & qmask), qv.y ^ (qsign & qmask), qv.z ^ (qsign & qmask),
+                           qv.w ^ (qsign & qmask));
+    }
+
+    // Block ids of 64 consecutive blocks sit in one VGPR (lane x holds block 64 * id_chunk + x)
+    // and are looked up with a lane shuffle. A 32-token tile never spans two such chunks.
+    const int last_blk = kmax >> prm.bs_log2;
+    int id_chunk = -1, ids = -1;
+    auto ensure_ids = [&](int tile) {
+      const int ch = ((tile * kTileTokens) >> prm.bs_log2) >> 6;
+      if (ch != id_chunk) {
+        id_chunk = ch;
+        const int x = 64 * ch + lane;
+        ids = bt[x <= last_blk ? x : 0];
+      }
+    };
+    auto block_at = [&](int pos) { return __shfl(ids, (pos >> prm.bs_log2) & 63, 64); };
 
     // Loader: piece r of this thread is token 16*th + c of the tile, 16-byte piece 4*dq + j.
-    uint4 kr[LD::LOADS], vr[LD::LOADS];
-    auto load_tile = [&](int tile) {
+    // Loads are unconditional (positions past kmax and bad block ids read row 0); the mask is
+    // applied when the tile goes to LDS, so the loads stay in flight meanwhile. Two tiles are in
+    // flight at once (register sets ra and rb, the loop unrolled by two).
+    struct TileRegs {
+      uint4 k[LD::LOADS], v[LD::LOADS];
+      uint32_t mask[LD::LOADS];
+      uint32_t vbits;  // bit t: token t is at or before kmax and its block id is valid
+    };
+    auto load_tile = [&](int tile, TileRegs& R) {
+      ensure_ids(tile);
 #pragma unroll
       for (int r = 0; r < LD::LOADS; ++r) {
         const int u = 4 * r + wave;
         const int t = 16 * (u & 1) + c, dp = 4 * (u >> 1) + j;
         const int pos = tile * kTileTokens + t;
-        // Unconditional loads (a branch around them would make the compiler wait for all
-        // loads in flight): positions past kmax and bad block ids read row 0 and become zeros.
-        const bool in_range = pos <= kmax;
-        const int blk = bt[in_range ? pos >> prm.bs_log2 : 0];
-        const bool ok = in_range && block_ok(blk);
+        const int blk = block_at(pos);
+        const bool ok = pos <= kmax && block_ok(blk);
         const size_t row = ok ? ((size_t)blk * Hkv + g) * BS + (pos & (BS - 1)) : 0;
-        const uint4 kv = prm.k_cache[row * ND + dp];
-        const uint4 vv = prm.v_cache[row * ND + dp];
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        kr[r] = ok ? kv : z;
-        vr[r] = ok ? vv : z;
+        R.mask[r] = ok ? 0xffffffffu : 0u;
+        R.k[r] = prm.k_cache[row * ND + dp];
+        R.v[r] = prm.v_cache[row * ND + dp];
       }
+      const int pos = tile * kTileTokens + n;
+      const bool ok = pos <= kmax && block_ok(block_at(pos));
+      R.vbits = (uint32_t)__ballot(ok);
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](int buf, const TileRegs& R) {
       unsigned char* kl = lds + buf * LD::BUF_BYTES;
       unsigned char* vl = kl + LD::K_BYTES;
 #pragma unroll
       for (int r = 0; r < LD::LOADS; ++r) {
         const int u = 4 * r + wave;
         const int t = 16 * (u & 1) + c, dp = 4 * (u >> 1) + j;
-        *reinterpret_cast<uint4*>(kl + k_row(t) * LD::K_STRIDE + 16 * dp) = kr[r];
+        *reinterpret_cast<uint4*>(kl + t * LD::K_STRIDE + 16 * dp) = mask4(R.k[r], R.mask[r]);
         const int col = vt_col(t);
-        const uint32_t w[4] = {vr[r].x, vr[r].y, vr[r].z, vr[r].w};
+        const uint4 vm = mask4(R.v[r], R.mask[r]);
+        const uint32_t w[4] = {vm.x, vm.y, vm.z, vm.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int d = 8 * dp + e;
@@ -211,97 +251,112 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillParams prm) {
         }
       }
     };
-    // Block id of the lane's 8 score tokens (8-aligned, so one block for block_size >= 8).
-    auto lane_block = [&](int tile) {
-      const int pos = tile * kTileTokens + 8 * j;
-      const int blk = bt[pos <= kmax ? pos >> prm.bs_log2 : 0];
-      return pos <= kmax ? blk : -1;
+
+    auto compute = [&](int it, uint32_t vbits) {
+      const unsigned char* kl = lds + (it & 1) * LD::BUF_BYTES;
+      const unsigned char* vl = kl + LD::K_BYTES;
+      // S^T[32 tokens x 32 rows] = K . Q^T (one accumulation chain; back-to-back MFMAs on the
+      // same accumulator are forwarded).
+      float16_t sa = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(kl + n * LD::K_STRIDE + 16 * (2 * ks + hl));
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), as_bf16x8(qop[ks]), sa, 0, 0, 0);
+      }
+      // Tokens this row may see in the tile, as a bit mask (no per-score branches): valid
+      // positions (vbits) up to the row's own position, none for rows outside the chunk. Tiles
+      // that every row of the wavefront sees whole skip the masking.
+      const int lim = pos_c - it * kTileTokens + 1;  // tokens 0 .. lim-1 are causal for this row
+      const uint32_t causal = lim >= 32 ? 0xffffffffu : lim <= 0 ? 0u : (1u << lim) - 1u;
+      const uint32_t allowed = (row_valid ? vbits & causal : 0u) >> (4 * hl);
+      float sc[16];
+      if (__all(allowed == (0xffffffffu >> (4 * hl)))) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[r] = sa[r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 8 * (r >> 2) + (r & 3);  // score_token(r, hl) - 4 hl
+          sc[r] = (allowed >> t) & 1u ? sa[r] : -INFINITY;
+        }
+      }
+      // Max of the raw scores, then in scaled log2 units (the factor is positive).
+      float mt = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[r]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * sl2;
+      // Lazy rescale: the reference max of a row moves only when the tile max exceeds it by
+      // more than kRescaleLog2 (or on the row's first finite score). Weights are then at most
+      // 2^kRescaleLog2, and the common factor cancels in the final division by l.
+      const bool bump = mt > m_run + kRescaleLog2;
+      if (__any(bump)) {
+        // 0 on a row's first finite max; 1 for rows that keep theirs (also those still at
+        // -inf, where m_run - m_run would be NaN).
+        const float alpha = bump ? fast_exp2(m_run - mt) : 1.f;
+        l_part *= alpha;
+#pragma unroll
+        for (int md = 0; md < MD; ++md) acc[md] *= alpha;
+        m_run = bump ? mt : m_run;
+      }
+      const float ms = m_run == -INFINITY ? 0.f : m_run;
+      bf16x8_t pb[2];
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(sc[r], sl2, -ms));
+        psum += p;
+        pb[r >> 3][r & 7] = (__bf16)p;
+      }
+      l_part += psum;
+      // O^T[32 d x 32 rows] += V^T[32 d x 16 tokens] . P^T[16 tokens x 32 rows], two token
+      // halves u per d block.
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        const int d = 32 * md + n;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const uint4 va = *reinterpret_cast<const uint4*>(vl + d * LD::VT_STRIDE + 16 * ((2 * u + hl) ^ vt_swz(d)));
+          acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), pb[u], acc[md], 0, 0, 0);
+        }
+      }
     };
 
-    load_tile(0);
-    int lb = lane_block(0);
-    store_tile(0);
-    __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-      const int buf = it & 1;
-      const bool has_next = it + 1 < ntiles;
-      int lb_next = -1;
-      if (has_next) {
-        load_tile(it + 1);
-        lb_next = lane_block(it + 1);
-      }
-      if (it < wave_tiles) {
-        const unsigned char* kl = lds + buf * LD::BUF_BYTES;
-        const unsigned char* vl = kl + LD::K_BYTES;
-        float4_t s[2] = {float4_t{0.f, 0.f, 0.f, 0.f}, float4_t{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const uint4 ka = *reinterpret_cast<const uint4*>(kl + (16 * h + c) * LD::K_STRIDE + 16 * (4 * kk + j));
-            s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(qop[kk]), s[h], 0, 0, 0);
-          }
-        }
-        // Lane's tokens: 8j + 2i + h of the tile (score s[h][i]).
-        const int base = it * kTileTokens + 8 * j;
-        const bool blk_ok = block_ok(lb);
-        float sc[2][4];
-        float mt = -INFINITY;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool ok = row_valid && blk_ok && base + 2 * i + h <= pos_c;
-            sc[h][i] = ok ? s[h][i] * prm.scale_log2e : -INFINITY;
-            mt = fmaxf(mt, sc[h][i]);
-          }
-        }
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const float m_new = fmaxf(m_run, mt);
-        const float ms = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - ms);
-        const bool grew = m_new != m_run;
-        m_run = m_new;
-        bf16x8_t pb;
-        float psum = 0.f;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p = fast_exp2(sc[h][i] - ms);
-            psum += p;
-            pb[4 * h + i] = (__bf16)p;
-          }
-        }
-        l_part = l_part * alpha + psum;
-        if (__any(grew)) {
-#pragma unroll
-          for (int md = 0; md < MD; ++md) acc[md] *= alpha;
-        }
-#pragma unroll
-        for (int md = 0; md < MD; ++md) {
-          const int d = 16 * md + c;
-          const uint4 va = *reinterpret_cast<const uint4*>(vl + d * LD::VT_STRIDE + 16 * (j ^ vt_swz(d)));
-          acc[md] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), pb, acc[md], 0, 0, 0);
-        }
-      }
-      if (has_next) store_tile(buf ^ 1);
+    // One step: tile it+2 starts loading into `fut`, tile it is processed from LDS, tile it+1
+    // (loaded one step earlier into `nxt`) goes to the other LDS buffer.
+    uint32_t vbits = 0;
+    auto step = [&](int it, TileRegs& nxt, TileRegs& fut) {
+      if (it + 2 < ntiles) load_tile(it + 2, fut);
+      if (it < wave_tiles) compute(it, vbits);
+      if (it + 1 < ntiles) store_tile((it + 1) & 1, nxt);
       __syncthreads();
-      lb = lb_next;
+      vbits = nxt.vbits;
+    };
+
+    TileRegs ra, rb;
+    load_tile(0, ra);
+    store_tile(0, ra);
+    vbits = ra.vbits;
+    if (ntiles > 1) load_tile(1, ra);
+    __syncthreads();
+    for (int it = 0; it < ntiles; it += 2) {
+      step(it, ra, rb);
+      if (it + 1 >= ntiles) break;
+      step(it + 1, rb, ra);
     }
   }
 
-  float l_tot = l_part + __shfl_xor(l_part, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
+  const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
   if (!row_exists) return;
   const float inv = row_valid && l_tot > 0.f ? 1.f / l_tot : 0.f;
-  // acc[md][e] is O[row c][16md + 4j + e].
+  // acc[md][r] is O[row n][32md + 8(r/4) + 4hl + r%4]: four runs of 4 values per d block.
   uint2* orow = reinterpret_cast<uint2*>(prm.out + out_row * ND);
 #pragma unroll
   for (int md = 0; md < MD; ++md) {
-    const float4_t o = acc[md] * inv;
-    orow[4 * md + j] = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float* o = reinterpret_cast<const float*>(&acc[md]) + 4 * q4;
+      orow[8 * md + 2 * q4 + hl] = make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
+    }
   }
 }
 

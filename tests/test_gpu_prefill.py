@@ -4,7 +4,7 @@ MI355X).
 The append must reproduce the oracle's pools bit for bit (only the chunk's slots change, the NaN
 poison elsewhere stays). The attention output is compared element by element with the fp64
 oracle at the bf16 bar (2e-2 absolute + 2e-2 relative); rows past chunk_lens[b] must be exactly
-zero. Shapes span several 64-row workgroups and 32-token key tiles with ragged tails, GQA groups
+zero. Shapes span several 128-row workgroups and 32-token key tiles with ragged tails, GQA groups
 that do and do not divide 16 (1, 3, 4, 6, 8, 12), head_dim 64/128, block_size 8/16/32, chunks
 that start at 0 or deep into a cached prefix, empty chunks and sequences outside the valid range.
 The Qwen3-8B 512-token chunk workload (the timed one) is checked in full for the append and on
@@ -103,6 +103,24 @@ def test_prefill_matches_oracle(shape):
                         block_size=BS, chunk=C, start_pos=sp, chunk_lens=cl, max_blocks_per_seq=mbps,
                         seed=hash(shape) % 1000)
     _full_check(w, f"Hq{Hq} Hkv{Hkv} D{D} BS{BS} C{C}")
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
+def test_prefill_scale_sign_and_zero(scale):
+    # A negative scale (q negated inside the kernel), scale 0 (uniform weights over the visible
+    # keys) and a large one (sharp softmax, many rescales).
+    w = PrefillWorkload(name="t", description="", dtype="bf16", num_q_heads=8, num_kv_heads=2, head_dim=128,
+                        block_size=16, chunk=40, start_pos=(0, 70), chunk_lens=(40, 29), max_blocks_per_seq=8,
+                        seed=21)
+    log(f"[gpu] prefill scale={scale}")
+    case = make_prefill_case(w)
+    kp, vp = oracle.kv_append_chunk(case.k_cache, case.v_cache, case.k_src, case.v_src, case.block_tables,
+                                    case.start_pos, case.chunk_lens, w.block_size)
+    exp = oracle.paged_prefill_attention(case.q, kp, vp, case.block_tables, case.start_pos, case.chunk_lens, scale,
+                                         w.block_size, "bf16")
+    dev = _to_dev(case)
+    out = _run(dev, scale)
+    assert_close(as_f64(out), exp, *TOL["bf16"], f"prefill scale={scale}")
 
 
 def test_invalid_sequences_get_zero_rows_and_no_append():
