@@ -7,7 +7,7 @@
 // attention with native GQA. Here a chunk row i of sequence b sits at position p = start_pos[b] + i
 // and sees the keys at positions 0..p (the causal mask aligned to the end of the cached range).
 //
-// Attention kernel. A workgroup of four wavefronts owns 128 consecutive "rows" of one
+// Attention kernel. A workgroup of eight wavefronts owns 256 consecutive "rows" of one
 // (sequence, kv head): row rho = i * G + r is chunk position i of query head g * G + r (G query
 // heads per kv head), so one K/V tile in LDS serves every head of the group. Each wavefront
 // owns 32 rows (one per lane column n = lane % 32) and walks the 32-token key tiles up to its
@@ -85,7 +85,7 @@ typedef float __attribute__((ext_vector_type(16))) float16_t;
 
 constexpr int kTileTokens = 32;
 constexpr int kRowsPerWave = 32;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kRowsPerGroup = kRowsPerWave * kWaves;
 constexpr float kRescaleLog2 = 8.f;  // weights stay below 2^8 between rescales
 
@@ -97,8 +97,15 @@ struct PrefillLds {
   static constexpr int VT_STRIDE = 2 * kTileTokens;      // one d row of V^T (bytes)
   static constexpr int VT_BYTES = D * VT_STRIDE;
   static constexpr int BUF_BYTES = K_BYTES + VT_BYTES;
-  static constexpr int LOADS = kTileTokens * ND / (64 * kWaves);  // 16-byte pieces per thread per tile
+  // 16-byte pieces per thread per tile (D = 64: the upper half of the wavefronts loads nothing).
+  static constexpr int LOADS = (kTileTokens * ND + 64 * kWaves - 1) / (64 * kWaves);
 };
+
+// (x in this lane, x in lane l ^ 32), in either order: one v_permlane32_swap, no LDS.
+__device__ __forceinline__ float2 with_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 __device__ __forceinline__ uint4 mask4(const uint4 v, uint32_t m) {
   return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
@@ -113,7 +120,7 @@ __device__ __forceinline__ int vt_col(int t) { return 8 * (2 * (t >> 4) + ((t >>
 __device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 3)) & 3; }
 
 template <int D>
-__global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillParams prm) {
+__global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParams prm) {
   using LD = PrefillLds<D>;
   constexpr int ND = LD::ND;
   constexpr int KS = D / 16;  // score steps (16 d each)
@@ -191,8 +198,9 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillParams prm) {
                            qv.w ^ (qsign & qmask));
     }
 
-    // Block ids of 64 consecutive blocks sit in one VGPR (lane x holds block 64 * id_chunk + x)
-    // and are looked up with a lane shuffle. A 32-token tile never spans two such chunks.
+    // Block ids of 64 consecutive blocks sit in one VGPR (lane x holds block 64 * id_chunk + x);
+    // a 32-token tile covers at most four of them, never across two chunks, and reads them as
+    // scalars (readlane), so no lookup goes through LDS.
     const int last_blk = kmax >> prm.bs_log2;
     int id_chunk = -1, ids = -1;
     auto ensure_ids = [&](int tile) {
@@ -203,7 +211,7 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillParams prm) {
         ids = bt[x <= last_blk ? x : 0];
       }
     };
-    auto block_at = [&](int pos) { return __shfl(ids, (pos >> prm.bs_log2) & 63, 64); };
+    auto block_id = [&](int bi) { return __builtin_amdgcn_readlane(ids, bi & 63); };
 
     // Loader: piece r of this thread is token 16*th + c of the tile, 16-byte piece 4*dq + j.
     // Loads are unconditional (positions past kmax and bad block ids read row 0); the mask is
@@ -216,21 +224,30 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillParams prm) {
     };
     auto load_tile = [&](int tile, TileRegs& R) {
       ensure_ids(tile);
+      const int t0 = tile * kTileTokens;
 #pragma unroll
       for (int r = 0; r < LD::LOADS; ++r) {
         const int u = 4 * r + wave;
-        const int t = 16 * (u & 1) + c, dp = 4 * (u >> 1) + j;
-        const int pos = tile * kTileTokens + t;
-        const int blk = block_at(pos);
-        const bool ok = pos <= kmax && block_ok(blk);
-        const size_t row = ok ? ((size_t)blk * Hkv + g) * BS + (pos & (BS - 1)) : 0;
+        const int th = u & 1, dp = 4 * (u >> 1) + j;
+        const int t = 16 * th + c;
+        const int pos = t0 + t;
+        // The 16 tokens of this piece row lie in one block, or two for block_size 8.
+        const int bi = (t0 + 16 * th) >> prm.bs_log2;
+        const int blk = prm.bs_log2 == 3 && c >= 8 ? block_id(bi + 1) : block_id(bi);
+        const bool ok = pos <= kmax && block_ok(blk) && dp < ND;
+        const size_t row = ok ? (((size_t)blk * Hkv + g) * BS + (pos & (BS - 1))) * ND + dp : 0;
         R.mask[r] = ok ? 0xffffffffu : 0u;
-        R.k[r] = prm.k_cache[row * ND + dp];
-        R.v[r] = prm.v_cache[row * ND + dp];
+        R.k[r] = prm.k_cache[row];
+        R.v[r] = prm.v_cache[row];
       }
-      const int pos = tile * kTileTokens + n;
-      const bool ok = pos <= kmax && block_ok(block_at(pos));
-      R.vbits = (uint32_t)__ballot(ok);
+      // Validity bits of the tile, computed on the scalar unit.
+      uint32_t bits = 0;
+      const int nb = kTileTokens >> prm.bs_log2;
+      const int b0 = t0 >> prm.bs_log2;
+      for (int k = 0; k < nb; ++k)
+        if (block_ok(block_id(b0 + k))) bits |= (BS == 32 ? 0xffffffffu : ((1u << BS) - 1u)) << (k * BS);
+      const int lim = kmax - t0 + 1;
+      R.vbits = lim >= 32 ? bits : bits & ((1u << lim) - 1u);
     };
     auto store_tile = [&](int buf, const TileRegs& R) {
       unsigned char* kl = lds + buf * LD::BUF_BYTES;
@@ -239,6 +256,7 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillParams prm) {
       for (int r = 0; r < LD::LOADS; ++r) {
         const int u = 4 * r + wave;
         const int t = 16 * (u & 1) + c, dp = 4 * (u >> 1) + j;
+        if (dp >= ND) continue;  // (a whole wavefront)
         *reinterpret_cast<uint4*>(kl + t * LD::K_STRIDE + 16 * dp) = mask4(R.k[r], R.mask[r]);
         const int col = vt_col(t);
         const uint4 vm = mask4(R.v[r], R.mask[r]);
@@ -284,7 +302,8 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillParams prm) {
       float mt = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * sl2;
+      const float2 mp = with_other_half(mt);
+      mt = fmaxf(mp.x, mp.y) * sl2;
       // Lazy rescale: the reference max of a row moves only when the tile max exceeds it by
       // more than kRescaleLog2 (or on the row's first finite score). Weights are then at most
       // 2^kRescaleLog2, and the common factor cancels in the final division by l.
@@ -345,7 +364,8 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillParams prm) {
     }
   }
 
-  const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
+  const float2 lp = with_other_half(l_part);
+  const float l_tot = lp.x + lp.y;
   if (!row_exists) return;
   const float inv = row_valid && l_tot > 0.f ? 1.f / l_tot : 0.f;
   // acc[md][r] is O[row n][32md + 8(r/4) + 4hl + r%4]: four runs of 4 values per d block.
