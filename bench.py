@@ -15,6 +15,10 @@ Prints ONE JSON line on stdout (diagnostics go to stderr):
                 source changed since the counters were taken
   cpu_baseline  the fp64 oracle timed on the host over a bounded sample of the same workload;
                 its output is also compared with the GPU's for those sequences
+  self_checks   block-permutation invariance (bitwise) and a length-1 sequence returning its V row
+                exactly, run on every bench run; a failure makes the exit status 3
+  extra rows    other decode workloads, KV block swap, chunked prefill (its own MFMA roofline),
+                and HIP-graph replay (see the functions below)
 
 Inputs are generated once and resident in HBM before timing. The pools exist in R copies
 (default: enough that R x pool > 3 GB), and step k reads copy k % R. Each step therefore
@@ -211,10 +215,53 @@ def run_workload(w, P: int, fused: bool, K: int, warmup: int, copies=None):
     for i in range(K):
         one_step(i, ev[i])
     torch.cuda.synchronize()
-    decode_ms_mean = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    decode_ms_mean = float(np.mean(launch_ms))
     out = steps[(K - 1) % R].out.float().cpu().double().numpy()
     del steps, pools, dev
-    return {"case": case, "R": R, "ms_step": ms_step, "decode_ms_mean": decode_ms_mean, "out": out}
+    return {"case": case, "R": R, "ms_step": ms_step, "decode_ms_mean": decode_ms_mean, "out": out,
+            "launch_us_p10_p50_p90": [round(float(np.percentile(launch_ms, q)) * 1e3, 2) for q in (10, 50, 90)]}
+
+
+def self_checks(P: int) -> dict:
+    """Run-to-run checks of the decode step that need no oracle (a fast but wrong kernel fails
+    them): (1) re-placing every pool block by a random permutation of the pool ids, with the
+    block table rewritten to match, gives bitwise the same output; (2) a sequence of length 1
+    returns exactly its V row. Qwen3-8B head shape, lengths 1, 100, 700 and 2049, the bench's
+    partition size, the fused append + decode step."""
+    import torch
+
+    import paged_kv_decode_xs_amd as xs
+    import workloads as wl
+    from workloads.device import case_to_device
+
+    w = wl.Workload(name="self_check", description="", dtype="bf16", batch=4, num_q_heads=32, num_kv_heads=8,
+                    head_dim=128, block_size=16, ctx=("fixed", [1, 100, 700, 2049]), num_blocks=None,
+                    max_blocks_per_seq=256, values="normal", seed=7, partition_size=P)
+    case = wl.make_case(w)
+
+    def run(c):
+        dev = case_to_device(c, "cuda:0")
+        step = xs.DecodeStep(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["context_lens"],
+                             dev["k_new"], dev["v_new"], w.scale, partition_size=P, max_context_len=2049, fused=True)
+        step.run()
+        torch.cuda.synchronize()
+        return step.out.view(torch.int16).cpu().numpy()
+
+    out1 = run(case)
+    rng = np.random.default_rng(8)
+    perm = rng.permutation(case.num_blocks)
+    moved = wl.Case(workload=w, q=case.q, k_new=case.k_new, v_new=case.v_new,
+                    k_cache=np.empty_like(case.k_cache), v_cache=np.empty_like(case.v_cache),
+                    block_tables=np.where(case.block_tables >= 0, perm[np.maximum(case.block_tables, 0)], -1)
+                    .astype(np.int32), context_lens=case.context_lens)
+    moved.k_cache[perm] = case.k_cache
+    moved.v_cache[perm] = case.v_cache
+    out2 = run(moved)
+    G = w.num_q_heads // w.num_kv_heads
+    v0 = case.v_new[0].view(np.int16)  # sequence 0 has length 1: its only token is the appended one
+    l1 = all(np.array_equal(out1[0, h], v0[h // G]) for h in range(w.num_q_heads))
+    return {"permutation_invariance_bitwise": bool(np.array_equal(out1, out2)), "length1_out_equals_v_bitwise": l1}
 
 
 # Launch-bound workloads timed eagerly and as a replayed HIP graph (xs_step_graph_*), as a stack of
@@ -347,8 +394,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 def prefill_row(name: str = "qwen3_8b_prefill_c512", reps: int = 20) -> dict:
     """Chunked prefill on the Qwen3-8B shape: the multi-token append and the causal attention of
-    the chunk, each timed alone (HIP events around single launches on the launch stream, median
-    of `reps`). The attention is a dense contraction on the matrix cores: its algorithmic flops
+    the chunk, each timed alone (HIP events on the launch stream, median of `reps`: around one
+    attention launch, around 20 back-to-back append launches). The attention is a dense contraction on the matrix cores: its algorithmic flops
     (4 * head_dim per (query head, chunk row, visible key)) over its time, against the bf16 dense
     MFMA peak. The append moves bytes: read + write of every chunk row, against HBM peak."""
     import torch
@@ -383,7 +430,12 @@ def prefill_row(name: str = "qwen3_8b_prefill_c512", reps: int = 20) -> dict:
             ts.append(a.elapsed_time(b))
         return float(np.median(ts))
 
-    append_ms = med(lambda: xs.xs_kv_append_chunk(ks, vs, kc, vc, bt, sp, cl, stream=stream))
+    # The append is a few microseconds: time 20 back-to-back launches per event pair (an event pair
+    # around a single launch of this size adds about as much as the launch itself).
+    def append20():
+        for _ in range(20):
+            xs.xs_kv_append_chunk(ks, vs, kc, vc, bt, sp, cl, stream=stream)
+    append_ms = med(append20) / 20
     attn_ms = med(lambda: xs.xs_paged_attn_prefill(q, kc, vc, bt, sp, cl, w.scale, out=out, stream=stream))
     finite = bool(torch.isfinite(out.float()).all().item())
     flops = w.attention_flops()
@@ -394,10 +446,17 @@ def prefill_row(name: str = "qwen3_8b_prefill_c512", reps: int = 20) -> dict:
         "workload": w.name,
         "description": w.description,
         "chunk_rows": int(case.chunk_lens.sum()),
-        "attention_flops": flops,
-        "attention_us": round(attn_ms * 1e3, 2),
-        "attention_TFLOPs": round(tflops, 2),
-        "attention_frac_of_bf16_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "paged_prefill_kernel",
+            "algorithmic_flops_per_launch": flops,
+            "median_launch_us": round(attn_ms * 1e3, 2),
+        },
         "append_bytes": ab,
         "append_us": round(append_ms * 1e3, 2),
         "append_GBps": round(gbs, 2),
@@ -449,6 +508,8 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed work, copy a 1 GiB buffer 5 times with torch (a plain copy kernel of "
                          "known size, to calibrate rocprofv3's FETCH_SIZE/WRITE_SIZE)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the chunked-prefill row (append + attention) and print its JSON line")
     ap.add_argument("--no-fuse", action="store_true",
                     help="issue xs_kv_append and xs_paged_attn_decode separately instead of the fused call")
     args = ap.parse_args()
@@ -468,6 +529,9 @@ def main() -> int:
         return 1
     torch.cuda.set_device(0)
     xs.load_library()  # raises if libxs.so is missing: there is no fallback path
+    if args.prefill_only:
+        print(json.dumps({"chunked_prefill": prefill_row(reps=max(args.steps, 5))}), flush=True)
+        return 0
 
     w = wl.WORKLOADS[args.workload]
     P = w.partition_size if args.partition is None else args.partition
@@ -551,7 +615,9 @@ def main() -> int:
             "algorithmic_bytes_per_launch": decode_bytes,
             "traffic_bytes_per_launch": traffic_bytes,
             "mean_launch_us": round(decode_ms_mean * 1e3, 2),
+            "launch_us_p10_p50_p90": r["launch_us_p10_p50_p90"],
         },
+        "self_checks": self_checks(P),
     }
     if not args.no_cpu_baseline:
         cpu, parity = cpu_baseline(case, r["out"], args.cpu_budget)
@@ -574,7 +640,10 @@ def main() -> int:
         result["graph_replay"] = [graph_row(wl.WORKLOADS[name], layers, min(K, 50), min(args.warmup, 5))
                                   for name, layers in GRAPH_WORKLOADS]
     print(json.dumps(result), flush=True)
-    return 0 if result.get("parity_vs_oracle", {}).get("out_of_tolerance", 0) == 0 else 3
+    checks_ok = all(result["self_checks"].values())
+    if not checks_ok:
+        log(f"[bench] SELF-CHECK FAILURE: {result['self_checks']}")
+    return 0 if result.get("parity_vs_oracle", {}).get("out_of_tolerance", 0) == 0 and checks_ok else 3
 
 
 if __name__ == "__main__":
