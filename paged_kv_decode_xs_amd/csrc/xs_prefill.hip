@@ -83,7 +83,7 @@ struct PrefillParams {
 
 typedef float __attribute__((ext_vector_type(16))) float16_t;
 
-constexpr int kTileTokens = 32;
+constexpr int kTileTokens = 64;
 constexpr int kRowsPerWave = 32;
 constexpr int kWaves = 8;
 constexpr int kRowsPerGroup = kRowsPerWave * kWaves;
@@ -92,13 +92,14 @@ constexpr float kRescaleLog2 = 8.f;  // weights stay below 2^8 between rescales
 template <int D>
 struct PrefillLds {
   static constexpr int ND = D / 8;                       // 16-byte pieces per token row
-  static constexpr int K_STRIDE = 2 * D + 16;            // padded K row (bytes)
+  static constexpr int K_STRIDE = 2 * D;                 // K row (bytes); pieces XOR-swizzled
   static constexpr int K_BYTES = kTileTokens * K_STRIDE;
   static constexpr int VT_STRIDE = 2 * kTileTokens;      // one d row of V^T (bytes)
   static constexpr int VT_BYTES = D * VT_STRIDE;
   static constexpr int BUF_BYTES = K_BYTES + VT_BYTES;
-  // 16-byte pieces per thread per tile (D = 64: the upper half of the wavefronts loads nothing).
-  static constexpr int LOADS = (kTileTokens * ND + 64 * kWaves - 1) / (64 * kWaves);
+  static constexpr int LOADS = kTileTokens * ND / (64 * kWaves);  // 16-byte pieces per thread per tile
+  static_assert(LOADS * 64 * kWaves == kTileTokens * ND, "loader");
+  static_assert(2 * BUF_BYTES <= 65536, "LDS");
 };
 
 // (x in this lane, x in lane l ^ 32), in either order: one v_permlane32_swap, no LDS.
@@ -111,13 +112,17 @@ __device__ __forceinline__ uint4 mask4(const uint4 v, uint32_t m) {
   return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
 }
 
-// Score register r of lane half hl holds token 8(r/4) + 4hl + r%4 of the tile.
-__device__ __forceinline__ int score_token(int r, int hl) { return 8 * (r >> 2) + 4 * hl + (r & 3); }
+// 16-byte piece p of K row t sits at slot p ^ (t % 8): eight consecutive rows read at the same
+// piece hit eight different bank groups.
+__device__ __forceinline__ int k_off(int t, int p, int stride) { return t * stride + 16 * (p ^ (t & 7)); }
+// Score register r of chain h2 and lane half hl holds token 32h2 + 8(r/4) + 4hl + r%4 of the tile.
 // Column of token t in a V^T row. The 16-byte slot 2u + hl holds, in element order e = 0..7, the
-// tokens of score registers 8u .. 8u+7 of lane half hl: the B operand of P.V step u.
+// tokens of score registers 8(u%2) .. 8(u%2)+7 of chain u/2 and lane half hl: the B operand of
+// P.V step u.
 __device__ __forceinline__ int vt_col(int t) { return 8 * (2 * (t >> 4) + ((t >> 2) & 1)) + 4 * ((t >> 3) & 1) + (t & 3); }
-// Slot swizzle of V^T row d: conflict-free 16-byte reads of 8 consecutive d rows.
-__device__ __forceinline__ int vt_swz(int d) { return ((d >> 1) ^ (d >> 3)) & 3; }
+// Slot swizzle of V^T row d (eight 16-byte slots): conflict-free 16-byte reads of 8 consecutive
+// d rows, 2-way conflicts at most on the transposing 2-byte writes.
+__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
 
 template <int D>
 __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParams prm) {
@@ -220,44 +225,44 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
     struct TileRegs {
       uint4 k[LD::LOADS], v[LD::LOADS];
       uint32_t mask[LD::LOADS];
-      uint32_t vbits;  // bit t: token t is at or before kmax and its block id is valid
+      uint64_t vbits;  // bit t: token t is at or before kmax and its block id is valid
     };
     auto load_tile = [&](int tile, TileRegs& R) {
       ensure_ids(tile);
       const int t0 = tile * kTileTokens;
 #pragma unroll
       for (int r = 0; r < LD::LOADS; ++r) {
-        const int u = 4 * r + wave;
-        const int th = u & 1, dp = 4 * (u >> 1) + j;
+        const int u = kWaves * r + wave;
+        const int th = u & 3, dp = 4 * (u >> 2) + j;
         const int t = 16 * th + c;
         const int pos = t0 + t;
         // The 16 tokens of this piece row lie in one block, or two for block_size 8.
         const int bi = (t0 + 16 * th) >> prm.bs_log2;
         const int blk = prm.bs_log2 == 3 && c >= 8 ? block_id(bi + 1) : block_id(bi);
-        const bool ok = pos <= kmax && block_ok(blk) && dp < ND;
+        const bool ok = pos <= kmax && block_ok(blk);
         const size_t row = ok ? (((size_t)blk * Hkv + g) * BS + (pos & (BS - 1))) * ND + dp : 0;
         R.mask[r] = ok ? 0xffffffffu : 0u;
         R.k[r] = prm.k_cache[row];
         R.v[r] = prm.v_cache[row];
       }
       // Validity bits of the tile, computed on the scalar unit.
-      uint32_t bits = 0;
+      uint64_t bits = 0;
       const int nb = kTileTokens >> prm.bs_log2;
       const int b0 = t0 >> prm.bs_log2;
+      const uint64_t one_block = (1ull << BS) - 1ull;
       for (int k = 0; k < nb; ++k)
-        if (block_ok(block_id(b0 + k))) bits |= (BS == 32 ? 0xffffffffu : ((1u << BS) - 1u)) << (k * BS);
+        if (block_ok(block_id(b0 + k))) bits |= one_block << (k * BS);
       const int lim = kmax - t0 + 1;
-      R.vbits = lim >= 32 ? bits : bits & ((1u << lim) - 1u);
+      R.vbits = lim >= 64 ? bits : bits & ((1ull << lim) - 1ull);
     };
     auto store_tile = [&](int buf, const TileRegs& R) {
       unsigned char* kl = lds + buf * LD::BUF_BYTES;
       unsigned char* vl = kl + LD::K_BYTES;
 #pragma unroll
       for (int r = 0; r < LD::LOADS; ++r) {
-        const int u = 4 * r + wave;
-        const int t = 16 * (u & 1) + c, dp = 4 * (u >> 1) + j;
-        if (dp >= ND) continue;  // (a whole wavefront)
-        *reinterpret_cast<uint4*>(kl + t * LD::K_STRIDE + 16 * dp) = mask4(R.k[r], R.mask[r]);
+        const int u = kWaves * r + wave;
+        const int t = 16 * (u & 3) + c, dp = 4 * (u >> 2) + j;
+        *reinterpret_cast<uint4*>(kl + k_off(t, dp, LD::K_STRIDE)) = mask4(R.k[r], R.mask[r]);
         const int col = vt_col(t);
         const uint4 vm = mask4(R.v[r], R.mask[r]);
         const uint32_t w[4] = {vm.x, vm.y, vm.z, vm.w};
@@ -270,38 +275,45 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
       }
     };
 
-    auto compute = [&](int it, uint32_t vbits) {
+    auto compute = [&](int it, uint64_t vbits) {
       const unsigned char* kl = lds + (it & 1) * LD::BUF_BYTES;
       const unsigned char* vl = kl + LD::K_BYTES;
-      // S^T[32 tokens x 32 rows] = K . Q^T (one accumulation chain; back-to-back MFMAs on the
-      // same accumulator are forwarded).
-      float16_t sa = {};
+      // S^T[64 tokens x 32 rows] = K . Q^T as two independent chains (tokens 0-31 and 32-63;
+      // back-to-back MFMAs on the same accumulator are forwarded).
+      float16_t sa0 = {}, sa1 = {};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(kl + n * LD::K_STRIDE + 16 * (2 * ks + hl));
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), as_bf16x8(qop[ks]), sa, 0, 0, 0);
+        const uint4 k0 = *reinterpret_cast<const uint4*>(kl + k_off(n, 2 * ks + hl, LD::K_STRIDE));
+        const uint4 k1 = *reinterpret_cast<const uint4*>(kl + k_off(32 + n, 2 * ks + hl, LD::K_STRIDE));
+        sa0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k0), as_bf16x8(qop[ks]), sa0, 0, 0, 0);
+        sa1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k1), as_bf16x8(qop[ks]), sa1, 0, 0, 0);
       }
       // Tokens this row may see in the tile, as a bit mask (no per-score branches): valid
       // positions (vbits) up to the row's own position, none for rows outside the chunk. Tiles
       // that every row of the wavefront sees whole skip the masking.
       const int lim = pos_c - it * kTileTokens + 1;  // tokens 0 .. lim-1 are causal for this row
-      const uint32_t causal = lim >= 32 ? 0xffffffffu : lim <= 0 ? 0u : (1u << lim) - 1u;
-      const uint32_t allowed = (row_valid ? vbits & causal : 0u) >> (4 * hl);
-      float sc[16];
-      if (__all(allowed == (0xffffffffu >> (4 * hl)))) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sc[r] = sa[r];
-      } else {
+      const uint64_t causal = lim >= 64 ? ~0ull : lim <= 0 ? 0ull : (1ull << lim) - 1ull;
+      const uint64_t allowed = row_valid ? vbits & causal : 0ull;
+      float sc[32];
+      if (__all(allowed == ~0ull)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int t = 8 * (r >> 2) + (r & 3);  // score_token(r, hl) - 4 hl
-          sc[r] = (allowed >> t) & 1u ? sa[r] : -INFINITY;
+          sc[r] = sa0[r];
+          sc[16 + r] = sa1[r];
+        }
+      } else {
+        const uint32_t a0 = (uint32_t)allowed >> (4 * hl), a1 = (uint32_t)(allowed >> 32) >> (4 * hl);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 8 * (r >> 2) + (r & 3);  // token of register r, less 4 hl (and 32 h2)
+          sc[r] = (a0 >> t) & 1u ? sa0[r] : -INFINITY;
+          sc[16 + r] = (a1 >> t) & 1u ? sa1[r] : -INFINITY;
         }
       }
       // Max of the raw scores, then in scaled log2 units (the factor is positive).
       float mt = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[r]);
+      for (int r = 0; r < 32; ++r) mt = fmaxf(mt, sc[r]);
       const float2 mp = with_other_half(mt);
       mt = fmaxf(mp.x, mp.y) * sl2;
       // Lazy rescale: the reference max of a row moves only when the tile max exceeds it by
@@ -318,22 +330,22 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
         m_run = bump ? mt : m_run;
       }
       const float ms = m_run == -INFINITY ? 0.f : m_run;
-      bf16x8_t pb[2];
+      bf16x8_t pb[4];
       float psum = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < 32; ++r) {
         const float p = fast_exp2(fmaf(sc[r], sl2, -ms));
         psum += p;
         pb[r >> 3][r & 7] = (__bf16)p;
       }
       l_part += psum;
-      // O^T[32 d x 32 rows] += V^T[32 d x 16 tokens] . P^T[16 tokens x 32 rows], two token
-      // halves u per d block.
+      // O^T[32 d x 32 rows] += V^T[32 d x 16 tokens] . P^T[16 tokens x 32 rows], four token
+      // quarters u per d block.
 #pragma unroll
       for (int md = 0; md < MD; ++md) {
         const int d = 32 * md + n;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < 4; ++u) {
           const uint4 va = *reinterpret_cast<const uint4*>(vl + d * LD::VT_STRIDE + 16 * ((2 * u + hl) ^ vt_swz(d)));
           acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), pb[u], acc[md], 0, 0, 0);
         }
@@ -342,7 +354,7 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
 
     // One step: tile it+2 starts loading into `fut`, tile it is processed from LDS, tile it+1
     // (loaded one step earlier into `nxt`) goes to the other LDS buffer.
-    uint32_t vbits = 0;
+    uint64_t vbits = 0;
     auto step = [&](int it, TileRegs& nxt, TileRegs& fut) {
       if (it + 2 < ntiles) load_tile(it + 2, fut);
       if (it < wave_tiles) compute(it, vbits);
