@@ -351,6 +351,7 @@ DecodeParams make_params(const DecodeArgs& a, int heads_per_wave) {
   p.scale_log2e = a.scale * kLog2e;
   p.sinks = static_cast<const uint16_t*>(a.sinks);
   p.window = a.window;
+  p.batch = a.batch;
   p.out = a.out;
   p.part_o = a.part_o;
   p.part_m = a.part_m;

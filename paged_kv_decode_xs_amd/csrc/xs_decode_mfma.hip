@@ -2,7 +2,11 @@
 // 16/32). The per-tile math lives in xs_mfma_tile.h; this file walks the work items.
 //
 // A work item (sequence, kv head, head chunk, partition) goes to one workgroup of NW = 1, 2 or 4
-// wavefronts, chosen at launch so that the grid fills the GPU. The wavefronts take the item's
+// wavefronts, chosen at launch so that the grid fills the GPU. With split-K the grid has one
+// workgroup per possible item (max_partitions per sequence), but workgroup k takes the k-th item
+// that exists: each reads the batch's lengths, counts the partitions, and maps its id onto the
+// full partitions first (sequence-major), then every sequence's partial last one. The real items
+// thus fill the front of the grid, evenly over the CUs, and the ids past them leave at once. The wavefronts take the item's
 // 16-token tiles round-robin, each keeps its own online-softmax state, and they merge through
 // LDS at the end (max, rescale, add). K/V are read with nontemporal loads (each byte is used
 // once), and each wavefront loads its next tile into a second register set while it processes
@@ -25,19 +29,23 @@ namespace {
 #endif
 
 
+template <int D, int BS, int GC, int NW>
+constexpr int decode_smem_bytes() {
+  using TA = TileAttn<D, GC>;
+  constexpr int MERGE_FLOATS = TA::ACC * 4 * 64 + 2 * GC;  // one wavefront's (acc, m, l)
+  return NW * TA::STAGE_BYTES > (NW - 1) * MERGE_FLOATS * 4 ? NW * TA::STAGE_BYTES : (NW - 1) * MERGE_FLOATS * 4;
+}
+
+// One work item: partition p of (sequence b, kv head g, head chunk ch).
 template <int D, int BS, int GC, int NW, bool SW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(XS_DECODE_MIN_WAVES_PER_EU)))
-void paged_decode_mfma_kernel(const DecodeParams prm) {
+__device__ __forceinline__ void decode_item(const DecodeParams& prm, unsigned char* smem, const int p, const int b,
+                                            const int g, const int ch) {
   using TA = TileAttn<D, GC>;
   constexpr int KK = TA::KK, NH = TA::NH, HP = TA::HP, ROW16 = TA::ROW16, VL = TA::VL, ACC = TA::ACC;
   constexpr int TPB = BS / 16;  // tiles per block
   constexpr int MERGE_FLOATS = ACC * 4 * 64 + 2 * GC;  // one wavefront's (acc, m, l)
-  constexpr int SMEM = NW * TA::STAGE_BYTES > (NW - 1) * MERGE_FLOATS * 4 ? NW * TA::STAGE_BYTES
-                                                                          : (NW - 1) * MERGE_FLOATS * 4;
   constexpr float kNegInf = -INFINITY;
   static_assert(BS % 16 == 0, "block_size must hold whole 16-token tiles");
-
-  __shared__ __align__(16) unsigned char smem[SMEM];
 
   const int wave = NW > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   const int lane = threadIdx.x & 63;
@@ -47,19 +55,6 @@ void paged_decode_mfma_kernel(const DecodeParams prm) {
   const int max_blocks_per_seq = prm.max_blocks_per_seq;
   const int max_partitions = prm.max_partitions;
   const bool split = prm.part_blocks > 0;
-  const int np = split ? max_partitions : 1;
-  // Work items are numbered partition-major. The hardware deals workgroups round-robin to the
-  // eight XCDs, so neighbouring ids must carry similar work: every (sequence, kv head) has a
-  // first partition but only long sequences have late ones, and with the partition index
-  // outermost each XCD gets an even share of every partition depth.
-  unsigned wg = blockIdx.x;
-  const unsigned per_p = gridDim.x / (unsigned)np;  // batch * num_kv_heads * chunks
-  const int p = wg / per_p;
-  wg %= per_p;
-  const int ch = wg % prm.chunks;
-  wg /= prm.chunks;
-  const int g = wg % num_kv_heads;
-  const int b = wg / num_kv_heads;
   const int h0 = g * prm.group + ch * GC;
 
   const int L_in = prm.context_lens[b];
@@ -224,6 +219,80 @@ void paged_decode_mfma_kernel(const DecodeParams prm) {
       for (int hf = 0; hf < NH; ++hf) o[64 * hf + lane] = (uint16_t)f32_to_bf16_rne(st.acc[hp * NH + hf][i] * f);
     }
   }
+}
+
+// Partitions of sequence b that the split grid computes: full ones (part_blocks blocks) and a
+// partial last one. Partitions at or past max_partitions are not computed.
+template <int BS>
+__device__ __forceinline__ void seq_partitions(const DecodeParams& prm, int b, int& nfull, int& npartial) {
+  const int L = min(prm.context_lens[b], prm.max_blocks_per_seq * BS);
+  const int nblk = L > 0 ? (L + BS - 1) / BS : 0;
+  nfull = min(nblk / prm.part_blocks, prm.max_partitions);
+  npartial = nblk % prm.part_blocks != 0 && nblk / prm.part_blocks < prm.max_partitions ? 1 : 0;
+}
+
+// The k-th existing split item (full partitions first, sequence-major, then the partial ones):
+// sets b, p and seg (kv head * chunks + chunk); b = -1 when there are fewer than k + 1 items.
+template <int BS>
+__device__ __forceinline__ void dense_item(const DecodeParams& prm, int k, int& b, int& p, int& seg) {
+  const int lane = threadIdx.x & 63;
+  const int batch = prm.batch;
+  const int segs = prm.num_kv_heads * prm.chunks;
+  int F = 0;
+  for (int b0 = 0; b0 < batch; b0 += 64) {
+    int nf = 0, np1 = 0;
+    if (b0 + lane < batch) seq_partitions<BS>(prm, b0 + lane, nf, np1);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) nf += __shfl_xor(nf, off, 64);
+    F += nf * segs;
+  }
+  const bool full = k < F;
+  if (!full) k -= F;
+  b = -1;
+  p = 0;
+  seg = 0;
+  int base = 0;
+  for (int b0 = 0; b0 < batch && b < 0; b0 += 64) {
+    int nf = 0, np1 = 0;
+    if (b0 + lane < batch) seq_partitions<BS>(prm, b0 + lane, nf, np1);
+    const int own = (full ? nf : np1) * segs;
+    int incl = own;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    const unsigned long long hit = __ballot(b0 + lane < batch && base + incl > k);
+    if (hit) {
+      const int first = __builtin_ctzll(hit);
+      const int r = k - base - __shfl(incl - own, first, 64);
+      b = b0 + first;
+      p = full ? r / segs : __shfl(nf, first, 64);
+      seg = full ? r % segs : r;
+    } else {
+      base += __shfl(incl, 63, 64);
+    }
+  }
+  b = __builtin_amdgcn_readfirstlane(b);
+  p = __builtin_amdgcn_readfirstlane(p);
+  seg = __builtin_amdgcn_readfirstlane(seg);
+}
+
+template <int D, int BS, int GC, int NW, bool SW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(XS_DECODE_MIN_WAVES_PER_EU)))
+void paged_decode_mfma_kernel(const DecodeParams prm) {
+  __shared__ __align__(16) unsigned char smem[decode_smem_bytes<D, BS, GC, NW>()];
+  int b, p, seg;
+  if (prm.part_blocks > 0) {
+    dense_item<BS>(prm, blockIdx.x, b, p, seg);
+    if (b < 0) return;  // past the items that exist
+  } else {
+    // No split: one item per (sequence, kv head, chunk).
+    seg = blockIdx.x % (prm.chunks * prm.num_kv_heads);
+    b = blockIdx.x / (prm.chunks * prm.num_kv_heads);
+    p = 0;
+  }
+  decode_item<D, BS, GC, NW, SW>(prm, smem, p, b, seg / prm.chunks, seg % prm.chunks);
 }
 
 template <int D, int BS, int GC, bool SW>

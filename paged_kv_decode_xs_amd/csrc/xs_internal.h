@@ -49,6 +49,7 @@ struct DecodeParams {
   int num_q_heads, num_kv_heads, group, chunks, max_blocks_per_seq, num_blocks, part_blocks, max_partitions;
   const uint16_t* sinks;  // bf16 sink logit per query head, or null
   int window;             // 0: all positions
+  int batch;
 };
 
 DecodeParams make_params(const DecodeArgs& a, int heads_per_wave);

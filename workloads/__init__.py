@@ -123,7 +123,7 @@ WORKLOADS: Dict[str, Workload] = {
             "head_dim 128, context_lens uniform in [128,8192], block_size 16, pool 1.25x need",
             dtype="bf16", batch=64, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
             ctx=("uniform", 128, 8192), num_blocks=None, max_blocks_per_seq=512, values="normal",
-            seed=3, partition_size=768,
+            seed=3, partition_size=1024,
         ),
         Workload(
             name="qwen3_8b_b4_long",
