@@ -6,7 +6,8 @@
 // workgroup per possible item (max_partitions per sequence), but workgroup k takes the k-th item
 // that exists: each reads the batch's lengths, counts the partitions, and maps its id onto the
 // full partitions first (sequence-major), then every sequence's partial last one. The real items
-// thus fill the front of the grid, evenly over the CUs, and the ids past them leave at once. The wavefronts take the item's
+// thus fill the front of the grid, evenly over the CUs, and the ids past them leave at once.
+// Batches of more than 256 sequences keep partition-major ids. The wavefronts take the item's
 // 16-token tiles round-robin, each keeps its own online-softmax state, and they merge through
 // LDS at the end (max, rescale, add). K/V are read with nontemporal loads (each byte is used
 // once), and each wavefront loads its next tile into a second register set while it processes
@@ -221,6 +222,9 @@ __device__ __forceinline__ void decode_item(const DecodeParams& prm, unsigned ch
   }
 }
 
+// The dense order scans the batch's lengths in every workgroup: up to this many sequences.
+constexpr int kDenseMaxBatch = 256;
+
 // Partitions of sequence b that the split grid computes: full ones (part_blocks blocks) and a
 // partial last one. Partitions at or past max_partitions are not computed.
 template <int BS>
@@ -283,9 +287,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(XS_DECO
 void paged_decode_mfma_kernel(const DecodeParams prm) {
   __shared__ __align__(16) unsigned char smem[decode_smem_bytes<D, BS, GC, NW>()];
   int b, p, seg;
-  if (prm.part_blocks > 0) {
+  if (prm.part_blocks > 0 && prm.batch <= kDenseMaxBatch) {
     dense_item<BS>(prm, blockIdx.x, b, p, seg);
     if (b < 0) return;  // past the items that exist
+  } else if (prm.part_blocks > 0) {
+    // Large batches: partition-major ids (every workgroup would otherwise scan all lengths).
+    // Neighbouring ids then carry similar work, and every XCD gets each partition depth.
+    const int per_p = prm.batch * prm.num_kv_heads * prm.chunks;
+    p = blockIdx.x / per_p;
+    seg = blockIdx.x % (prm.chunks * prm.num_kv_heads);
+    b = (blockIdx.x % per_p) / (prm.chunks * prm.num_kv_heads);
   } else {
     // No split: one item per (sequence, kv head, chunk).
     seg = blockIdx.x % (prm.chunks * prm.num_kv_heads);

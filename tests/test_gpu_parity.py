@@ -163,3 +163,18 @@ def test_fused_append_is_bitwise_the_two_calls(dtype, Hq, Hkv, D, BS, lens, P):
         for name in ("k_cache", "v_cache"):
             assert torch.equal(a[name].view(view), b[name].view(view)), f"{name} differs (P={part})"
     log(f"[gpu] fused append: bitwise equal to append + decode for {dtype} D={D} BS={BS}")
+
+
+def test_split_order_for_large_and_small_batches():
+    # The split grid maps workgroup ids onto the partitions that exist (dense order) for batches
+    # of up to 256 sequences and keeps partition-major ids above that; both orders must give the
+    # oracle's result, with partitions past a sequence's end and empty sequences mixed in.
+    rng = np.random.default_rng(31)
+    for B in (256, 300):
+        lens = rng.integers(0, 400, B).tolist()
+        lens[3] = 0
+        lens[5] = 1
+        case = _shape_case("bf16", 8, 2, 64, 16, lens, seed=32 + B)
+        ref = OracleResult(case, 64)
+        check_case(case, 64, ref, check_pools=False, label=f"split order B={B}")
+        check_case(case, 64, ref, label=f"split order B={B} fused", fused=True)
