@@ -104,6 +104,17 @@ def algorithmic_bytes(case, partition: int):
     return {"kv": kv, "decode": decode, "reduce": reduce, "append": append, "step": decode + reduce + append}
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(case, gpu_out, budget_s: float):
     """Time the fp64 oracle over whole sequences until the time budget is used; compare outputs."""
     import oracle  # the oracle is test infrastructure; this leg is the only bench code that uses it
@@ -143,6 +154,8 @@ def cpu_baseline(case, gpu_out, budget_s: float):
                   f"({int(case.context_lens[:done].sum())} tokens, {kv_bytes / 1e6:.1f} MB of K+V), "
                   f"{elapsed:.2f} s; K+V bytes of the sample / oracle time",
         "seconds": round(elapsed, 3),
+        "cpu_model": _cpu_model(),
+        "host_cpus": os.cpu_count(),
     }, {"sequences_checked": done, "max_abs_err": max_err, "out_of_tolerance": bad}
 
 
@@ -216,10 +229,20 @@ def run_workload(w, P: int, fused: bool, K: int, warmup: int, copies=None):
         one_step(i, ev[i])
     torch.cuda.synchronize()
     launch_ms = [a.elapsed_time(b) for a, b in ev]
+    # Warm-cache reference: the same K steps, all on pool copy 0 (what the Infinity Cache keeps of
+    # it stays there between steps). Secondary to the rotated (cache-flushed) number above.
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        one_step(i * R)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_warm = start.elapsed_time(end) / K
     decode_ms_mean = float(np.mean(launch_ms))
     out = steps[(K - 1) % R].out.float().cpu().double().numpy()
     del steps, pools, dev
     return {"case": case, "R": R, "ms_step": ms_step, "decode_ms_mean": decode_ms_mean, "out": out,
+            "ms_step_warm": ms_warm,
             "launch_us_p10_p50_p90": [round(float(np.percentile(launch_ms, q)) * 1e3, 2) for q in (10, 50, 90)]}
 
 
@@ -602,6 +625,7 @@ def main() -> int:
         },
         "seqs_per_s": round(w.batch / (ms_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100 * kv_gbs / HBM_PEAK_GBS, 2),
+        "warm_cache_kv_GBps": round(ab["kv"] / (r["ms_step_warm"] * 1e-3) / 1e9, 2),
         "achievable_read_GBps": achievable,
         "pct_of_achievable_nontemporal_read": round(100 * kv_gbs / achievable["nontemporal"], 2),
         "roofline": {
