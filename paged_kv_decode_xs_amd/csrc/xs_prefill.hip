@@ -94,9 +94,8 @@ struct PrefillLds {
   static constexpr int ND = D / 8;                       // 16-byte pieces per token row
   static constexpr int K_STRIDE = 2 * D;                 // K row (bytes); pieces XOR-swizzled
   static constexpr int K_BYTES = kTileTokens * K_STRIDE;
-  static constexpr int VT_STRIDE = 2 * kTileTokens;      // one d row of V^T (bytes)
-  static constexpr int VT_BYTES = D * VT_STRIDE;
-  static constexpr int BUF_BYTES = K_BYTES + VT_BYTES;
+  static constexpr int V_BYTES = kTileTokens * K_STRIDE;  // V rows like K rows (own swizzle)
+  static constexpr int BUF_BYTES = K_BYTES + V_BYTES;
   static constexpr int LOADS = kTileTokens * ND / (64 * kWaves);  // 16-byte pieces per thread per tile
   static_assert(LOADS * 64 * kWaves == kTileTokens * ND, "loader");
   static_assert(2 * BUF_BYTES <= 65536, "LDS");
@@ -116,13 +115,20 @@ __device__ __forceinline__ uint4 mask4(const uint4 v, uint32_t m) {
 // piece hit eight different bank groups.
 __device__ __forceinline__ int k_off(int t, int p, int stride) { return t * stride + 16 * (p ^ (t & 7)); }
 // Score register r of chain h2 and lane half hl holds token 32h2 + 8(r/4) + 4hl + r%4 of the tile.
-// Column of token t in a V^T row. The 16-byte slot 2u + hl holds, in element order e = 0..7, the
-// tokens of score registers 8(u%2) .. 8(u%2)+7 of chain u/2 and lane half hl: the B operand of
-// P.V step u.
-__device__ __forceinline__ int vt_col(int t) { return 8 * (2 * (t >> 4) + ((t >> 2) & 1)) + 4 * ((t >> 3) & 1) + (t & 3); }
-// Slot swizzle of V^T row d (eight 16-byte slots): conflict-free 16-byte reads of 8 consecutive
-// d rows, 2-way conflicts at most on the transposing 2-byte writes.
-__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
+// V rows are stored like K rows (token-major, 2D bytes), 16-byte piece p of row t at slot
+// p ^ v_swz(t): eight consecutive rows written at one piece hit eight bank groups, and the four
+// rows of a transposing read (below) hit four different 32-byte ranges.
+__device__ __forceinline__ int v_swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes, lane i receives
+// element i % 4 of the 8-byte chunks addressed by lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4. With
+// lane j of the group addressing row t0 + j/4 at column c0 + 4 (j % 4), lane i receives rows
+// t0 .. t0+3 at column c0 + i.
+typedef short __attribute__((ext_vector_type(4))) short4_lds_t;
+typedef __attribute__((address_space(3))) unsigned char lds_byte;
+__device__ __forceinline__ short4_lds_t lds_read_tr16(lds_byte* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_lds_t*)p);
+}
 
 template <int D>
 __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParams prm) {
@@ -263,15 +269,7 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
         const int u = kWaves * r + wave;
         const int t = 16 * (u & 3) + c, dp = 4 * (u >> 2) + j;
         *reinterpret_cast<uint4*>(kl + k_off(t, dp, LD::K_STRIDE)) = mask4(R.k[r], R.mask[r]);
-        const int col = vt_col(t);
-        const uint4 vm = mask4(R.v[r], R.mask[r]);
-        const uint32_t w[4] = {vm.x, vm.y, vm.z, vm.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = 8 * dp + e;
-          const int off = d * LD::VT_STRIDE + 16 * ((col >> 3) ^ vt_swz(d)) + 2 * (col & 7);
-          *reinterpret_cast<uint16_t*>(vl + off) = (uint16_t)(e & 1 ? w[e >> 1] >> 16 : w[e >> 1] & 0xffffu);
-        }
+        *reinterpret_cast<uint4*>(vl + t * LD::K_STRIDE + 16 * (dp ^ v_swz(t))) = mask4(R.v[r], R.mask[r]);
       }
     };
 
@@ -340,14 +338,30 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
       }
       l_part += psum;
       // O^T[32 d x 32 rows] += V^T[32 d x 16 tokens] . P^T[16 tokens x 32 rows], four token
-      // quarters u per d block.
+      // quarters u per d block. The A operand of lane (n, hl) is V at d = 32md + n for the tokens
+      // of its weights: 16u + 4hl + 0..3 and 16u + 8 + 4hl + 0..3 (two transposing reads; lane j
+      // of each 16-lane group addresses row j/4 of the four, at d 32md + 16((lane/16)%2) + 4(j%4)).
+      // All rows a lane reads are 4hl + j/4 plus a multiple of 8, so they share one swizzle: the
+      // address is one per-lane base per d block plus a constant row offset.
+      const int jg = lane & 15;
+      const int dcol = 16 * ((lane >> 4) & 1) + 4 * (jg & 3);  // d within the 32-wide block
+      const int row_l = 4 * hl + (jg >> 2);
+      const int swz_l = v_swz(row_l);
 #pragma unroll
       for (int md = 0; md < MD; ++md) {
-        const int d = 32 * md + n;
+        const int d = 32 * md + dcol;
+        lds_byte* vb = (lds_byte*)vl + (row_l * LD::K_STRIDE + 16 * ((d >> 3) ^ swz_l) + (d & 7) * 2);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const uint4 va = *reinterpret_cast<const uint4*>(vl + d * LD::VT_STRIDE + 16 * ((2 * u + hl) ^ vt_swz(d)));
-          acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), pb[u], acc[md], 0, 0, 0);
+          const short4_lds_t lo = lds_read_tr16(vb + 16 * u * LD::K_STRIDE);
+          const short4_lds_t hi = lds_read_tr16(vb + (16 * u + 8) * LD::K_STRIDE);
+          const short4_t lo4 = __builtin_bit_cast(short4_t, lo), hi4 = __builtin_bit_cast(short4_t, hi);
+          const bf16x8_t va = __builtin_bit_cast(
+              bf16x8_t, make_uint4((uint16_t)lo4[0] | ((uint32_t)(uint16_t)lo4[1] << 16),
+                                   (uint16_t)lo4[2] | ((uint32_t)(uint16_t)lo4[3] << 16),
+                                   (uint16_t)hi4[0] | ((uint32_t)(uint16_t)hi4[1] << 16),
+                                   (uint16_t)hi4[2] | ((uint32_t)(uint16_t)hi4[3] << 16)));
+          acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[u], acc[md], 0, 0, 0);
         }
       }
     };
