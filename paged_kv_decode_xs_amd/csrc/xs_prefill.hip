@@ -10,20 +10,20 @@
 // Attention kernel. A workgroup of eight wavefronts owns 256 consecutive "rows" of one
 // (sequence, kv head): row rho = i * G + r is chunk position i of query head g * G + r (G query
 // heads per kv head), so one K/V tile in LDS serves every head of the group. Each wavefront
-// owns 32 rows (one per lane column n = lane % 32) and walks the 32-token key tiles up to its
+// owns 32 rows (one per lane column n = lane % 32) and walks the 64-token key tiles up to its
 // last row's position:
-//   scores  S^T[32 tokens x 32 rows] = K . Q^T with v_mfma_f32_32x32x16_bf16 (D/16 of them, q in
-//           registers). Lane l then holds 16 scores of row l%32 (tokens 8(r/4) + 4(l/32) + r%4):
-//           the row max and sum are a reduction over the lane's 16 values and one lane swap;
-//           the accumulator rescale is per lane.
-//   P.V     O^T[D x 32 rows] += V^T[D x 16] . P^T[16 x 32] with v_mfma_f32_32x32x16_bf16, two
-//           token halves per 32-wide d block. The B operand (P^T, rounded to bf16) is exactly
+//   scores  S^T[64 tokens x 32 rows] = K . Q^T as two independent chains of
+//           v_mfma_f32_32x32x16_bf16 (tokens 0-31 and 32-63, D/16 each, q in registers). Lane l
+//           then holds 32 scores of row l%32: the row max and sum are a reduction over the
+//           lane's values and one lane swap; the accumulator rescale is per lane.
+//   P.V     O^T[D x 32 rows] += V^T[D x 16] . P^T[16 x 32] with v_mfma_f32_32x32x16_bf16, four
+//           token quarters per 32-wide d block. The B operand (P^T, rounded to bf16) is exactly
 //           what the score MFMAs left in each lane. The A operand needs 8 tokens of one d per
-//           lane, so V is staged in LDS transposed ([d][token], 64 bytes per d row, 16-byte
-//           slots XOR-swizzled by d) and read back 16 bytes at a time.
+//           lane: V is staged in LDS token-major like K and read back with the transposing LDS
+//           read (ds_read_b64_tr_b16).
 // The next two tiles are loaded into registers while the current one is processed
-// (double-buffered LDS, one barrier per tile). Tokens past the causal limit of a row get score -inf; tiles past
-// the workgroup's last position are never loaded, and K/V of positions past it are zero.
+// (double-buffered LDS, one barrier per tile). Tokens past the causal limit of a row get score
+// -inf, and K/V of positions past the workgroup's last key or in a bad block are zero.
 #include <math.h>
 
 #include "xs_internal.h"
@@ -209,20 +209,16 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
                            qv.w ^ (qsign & qmask));
     }
 
-    // Block ids of 64 consecutive blocks sit in one VGPR (lane x holds block 64 * id_chunk + x);
-    // a 32-token tile covers at most four of them, never across two chunks, and reads them as
-    // scalars (readlane), so no lookup goes through LDS.
+    // The block ids of a tile (at most 8: 64 tokens, block_size >= 8) sit in one VGPR, lane x
+    // holding block 64 tile / BS + x % 8, and are read as scalars (readlane). They are loaded one
+    // step before the tile's own loads, and every step issues the same loads (tiles past the
+    // workgroup's keys read row 0 and are masked), so the waits for one tile never drain the
+    // loads of the next.
     const int last_blk = kmax >> prm.bs_log2;
-    int id_chunk = -1, ids = -1;
-    auto ensure_ids = [&](int tile) {
-      const int ch = ((tile * kTileTokens) >> prm.bs_log2) >> 6;
-      if (ch != id_chunk) {
-        id_chunk = ch;
-        const int x = 64 * ch + lane;
-        ids = bt[x <= last_blk ? x : 0];
-      }
+    auto tile_ids = [&](int tile) {
+      const int x = ((tile * kTileTokens) >> prm.bs_log2) + (lane & 7);
+      return bt[x <= last_blk ? x : 0];
     };
-    auto block_id = [&](int bi) { return __builtin_amdgcn_readlane(ids, bi & 63); };
 
     // Loader: piece r of this thread is token 16*th + c of the tile, 16-byte piece 4*dq + j.
     // Loads are unconditional (positions past kmax and bad block ids read row 0); the mask is
@@ -233,8 +229,8 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
       uint32_t mask[LD::LOADS];
       uint64_t vbits;  // bit t: token t is at or before kmax and its block id is valid
     };
-    auto load_tile = [&](int tile, TileRegs& R) {
-      ensure_ids(tile);
+    auto load_tile = [&](int tile, int ids, TileRegs& R) {
+      auto block_id = [&](int k) { return __builtin_amdgcn_readlane(ids, k); };
       const int t0 = tile * kTileTokens;
 #pragma unroll
       for (int r = 0; r < LD::LOADS; ++r) {
@@ -243,7 +239,7 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
         const int t = 16 * th + c;
         const int pos = t0 + t;
         // The 16 tokens of this piece row lie in one block, or two for block_size 8.
-        const int bi = (t0 + 16 * th) >> prm.bs_log2;
+        const int bi = (16 * th) >> prm.bs_log2;
         const int blk = prm.bs_log2 == 3 && c >= 8 ? block_id(bi + 1) : block_id(bi);
         const bool ok = pos <= kmax && block_ok(blk);
         const size_t row = ok ? (((size_t)blk * Hkv + g) * BS + (pos & (BS - 1))) * ND + dp : 0;
@@ -254,12 +250,11 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
       // Validity bits of the tile, computed on the scalar unit.
       uint64_t bits = 0;
       const int nb = kTileTokens >> prm.bs_log2;
-      const int b0 = t0 >> prm.bs_log2;
       const uint64_t one_block = (1ull << BS) - 1ull;
       for (int k = 0; k < nb; ++k)
-        if (block_ok(block_id(b0 + k))) bits |= one_block << (k * BS);
+        if (block_ok(block_id(k))) bits |= one_block << (k * BS);
       const int lim = kmax - t0 + 1;
-      R.vbits = lim >= 64 ? bits : bits & ((1ull << lim) - 1ull);
+      R.vbits = lim >= 64 ? bits : lim <= 0 ? 0ull : bits & ((1ull << lim) - 1ull);
     };
     auto store_tile = [&](int buf, const TileRegs& R) {
       unsigned char* kl = lds + buf * LD::BUF_BYTES;
@@ -366,27 +361,33 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
       }
     };
 
-    // One step: tile it+2 starts loading into `fut`, tile it is processed from LDS, tile it+1
-    // (loaded one step earlier into `nxt`) goes to the other LDS buffer.
+    // One step: the ids of tile it+3 and tile it+2 itself (into `fut`) start loading, tile it is
+    // processed from LDS, tile it+1 (loaded one step earlier into `nxt`) goes to the other LDS
+    // buffer.
     uint64_t vbits = 0;
-    auto step = [&](int it, TileRegs& nxt, TileRegs& fut) {
-      if (it + 2 < ntiles) load_tile(it + 2, fut);
+    auto step = [&](int it, TileRegs& nxt, TileRegs& fut, int& ids_now, int& ids_next) {
+      ids_next = tile_ids(it + 3);
+      load_tile(it + 2, ids_now, fut);
       if (it < wave_tiles) compute(it, vbits);
-      if (it + 1 < ntiles) store_tile((it + 1) & 1, nxt);
+      store_tile((it + 1) & 1, nxt);
       __syncthreads();
       vbits = nxt.vbits;
     };
 
     TileRegs ra, rb;
-    load_tile(0, ra);
+    int ida = tile_ids(0), idb;
+    load_tile(0, ida, ra);
     store_tile(0, ra);
     vbits = ra.vbits;
-    if (ntiles > 1) load_tile(1, ra);
+    // Same order of loads as in a step: the ids of tile 2 before the loads of tile 1.
+    idb = tile_ids(1);
+    ida = tile_ids(2);
+    load_tile(1, idb, ra);
     __syncthreads();
     for (int it = 0; it < ntiles; it += 2) {
-      step(it, ra, rb);
+      step(it, ra, rb, ida, idb);
       if (it + 1 >= ntiles) break;
-      step(it + 1, rb, ra);
+      step(it + 1, rb, ra, idb, ida);
     }
   }
 
