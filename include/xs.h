@@ -339,10 +339,10 @@ int xs_paged_attn_prefill(const void* q, const void* k_cache, const void* v_cach
 
 /*
  * Measurement aid, not part of the decode step: reads `bytes` (a multiple of 16) at `buf` with
- * 16-byte loads (nontemporal if `nontemporal` != 0) in a grid-stride loop, and writes at most
- * one word to `sink` (device memory, 4 bytes). Timing it gives the read rate that plain
- * streaming reaches on the device, the reference the decode kernel's bandwidth is compared
- * with. `buf` must be 16-byte aligned.
+ * 16-byte loads (nontemporal if `nontemporal` != 0), each workgroup taking whole 64 KiB chunks,
+ * and writes at most one word to `sink` (device memory, 4 bytes). Timing it gives the read rate
+ * that contiguous streaming reaches on the device, the reference the decode kernel's bandwidth
+ * is compared with. `buf` must be 16-byte aligned.
  */
 int xs_stream_read_probe(const void* buf, size_t bytes, unsigned* sink, int nontemporal, void* stream);
 
