@@ -415,10 +415,16 @@ def swap_row(reps: int = 10) -> dict:
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
+PREFILL_SPLITS = {"qwen3_8b_prefill_c512": (1024, 2048), "qwen3_8b_prefill_long16k": (1024, 2048, 4096)}
+
+
 def prefill_row(name: str = "qwen3_8b_prefill_c512", reps: int = 20) -> dict:
     """Chunked prefill on the Qwen3-8B shape: the multi-token append and the causal attention of
     the chunk, each timed alone (HIP events on the launch stream, median of `reps`: around one
-    attention launch, around 20 back-to-back append launches). The attention is a dense contraction on the matrix cores: its algorithmic flops
+    attention call, around 20 back-to-back append launches). The attention is timed whole
+    (xs_paged_attn_prefill) and with split-K over the key range (xs_paged_attn_prefill_split: the
+    attention kernel and the merge kernel) at the partition sizes of PREFILL_SPLITS; the roofline
+    object is the fastest of them. It is a dense contraction on the matrix cores: algorithmic flops
     (4 * head_dim per (query head, chunk row, visible key)) over its time, against the bf16 dense
     MFMA peak. The append moves bytes: read + write of every chunk row, against HBM peak."""
     import torch
@@ -459,8 +465,19 @@ def prefill_row(name: str = "qwen3_8b_prefill_c512", reps: int = 20) -> dict:
         for _ in range(20):
             xs.xs_kv_append_chunk(ks, vs, kc, vc, bt, sp, cl, stream=stream)
     append_ms = med(append20) / 20
-    attn_ms = med(lambda: xs.xs_paged_attn_prefill(q, kc, vc, bt, sp, cl, w.scale, out=out, stream=stream))
+    by_p = {0: med(lambda: xs.xs_paged_attn_prefill(q, kc, vc, bt, sp, cl, w.scale, out=out, stream=stream))}
     finite = bool(torch.isfinite(out.float()).all().item())
+    for P in PREFILL_SPLITS.get(name, ()):
+        NP = xs.num_partitions(bt.shape[1] * kc.shape[2], P)
+        po = torch.empty((*q.shape[:3], NP, q.shape[3]), dtype=torch.float32, device="cuda")
+        pml = torch.empty((*q.shape[:3], NP, 2), dtype=torch.float32, device="cuda")
+        out_s = torch.empty_like(q)
+        by_p[P] = med(lambda: xs.xs_paged_attn_prefill_split(q, kc, vc, bt, sp, cl, w.scale, P, out=out_s, part_o=po,
+                                                             part_ml=pml, stream=stream))
+        finite = finite and bool(torch.isfinite(out_s.float()).all().item())
+        del po, pml, out_s
+    best_p = min(by_p, key=by_p.get)
+    attn_ms = by_p[best_p]
     flops = w.attention_flops()
     tflops = flops / (attn_ms * 1e-3) / 1e12
     ab = w.append_bytes()
@@ -476,10 +493,12 @@ def prefill_row(name: str = "qwen3_8b_prefill_c512", reps: int = 20) -> dict:
             "unit": "TFLOP/s",
             "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": None,
-            "kernel": "paged_prefill_kernel",
+            "kernel": "paged_prefill_kernel" if best_p == 0 else
+                      f"paged_prefill_kernel + prefill_merge_kernel (split-K, partition_size {best_p})",
             "algorithmic_flops_per_launch": flops,
             "median_launch_us": round(attn_ms * 1e3, 2),
         },
+        "attention_us_by_partition_size": {str(k): round(v * 1e3, 2) for k, v in by_p.items()},
         "append_bytes": ab,
         "append_us": round(append_ms * 1e3, 2),
         "append_GBps": round(gbs, 2),
@@ -553,7 +572,9 @@ def main() -> int:
     torch.cuda.set_device(0)
     xs.load_library()  # raises if libxs.so is missing: there is no fallback path
     if args.prefill_only:
-        print(json.dumps({"chunked_prefill": prefill_row(reps=max(args.steps, 5))}), flush=True)
+        reps = max(args.steps, 5)
+        print(json.dumps({"chunked_prefill": prefill_row(reps=reps),
+                          "chunked_prefill_long": prefill_row("qwen3_8b_prefill_long16k", reps=reps)}), flush=True)
         return 0
 
     w = wl.WORKLOADS[args.workload]
@@ -661,6 +682,8 @@ def main() -> int:
         result["extra_workloads"] = rows
         result["kv_swap"] = swap_row()
         result["chunked_prefill"] = prefill_row()
+        torch.cuda.empty_cache()
+        result["chunked_prefill_long"] = prefill_row("qwen3_8b_prefill_long16k")
         result["graph_replay"] = [graph_row(wl.WORKLOADS[name], layers, min(K, 50), min(args.warmup, 5))
                                   for name, layers in GRAPH_WORKLOADS]
     print(json.dumps(result), flush=True)

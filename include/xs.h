@@ -338,6 +338,32 @@ int xs_paged_attn_prefill(const void* q, const void* k_cache, const void* v_cach
                           void* stream);
 
 /*
+ * Chunked prefill attention with split-K over the key range: the same result as
+ * xs_paged_attn_prefill (the same passage), computed in pieces so that the row blocks with the
+ * most keys (the chunks that start deepest into their sequence) are spread over more compute
+ * units. Row blocks of 256 (chunk row, query head) pairs of one kv head cut their keys into
+ * pieces of `partition_size` positions (piece j: positions [j P, (j+1) P)); a row block with a
+ * single piece writes `out` directly, the others leave, for every row and piece, the row's
+ * output over the piece's keys o_j (fp32) and (m_j, l_j) (m_j the reference max in scaled log2
+ * units, l_j the sum of 2^(s log2e - m_j) over those keys; m_j = -inf, l_j = 0, o_j = 0 for a
+ * piece with none of the row's keys). A second kernel, launched by this call on the same
+ * stream, merges them with the log-sum-exp identity (not on the pages: exact up to rounding):
+ *   M = max_j m_j,  w_j = l_j 2^(m_j - M),  out = sum_j w_j o_j / sum_j w_j.
+ * Arguments as xs_paged_attn_prefill, plus: part_o [batch, num_q_heads, chunk_size,
+ * max_partitions, head_dim] fp32 and part_ml [batch, num_q_heads, chunk_size, max_partitions, 2]
+ * fp32, device scratch owned by the caller (16- and 8-byte aligned; contents on entry are not
+ * read, on exit unspecified); partition_size a positive multiple of 64; max_partitions >=
+ * ceil(max_blocks_per_seq * block_size / partition_size) (XS_EINVAL otherwise). batch == 0 or
+ * chunk_size == 0 is a no-op.
+ */
+int xs_paged_attn_prefill_split(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, const int32_t* start_pos, const int32_t* chunk_lens,
+                                float scale, void* out, float* part_o, float* part_ml, int batch, int num_q_heads,
+                                int num_kv_heads, int head_dim, int chunk_size, int block_size,
+                                int max_blocks_per_seq, int num_blocks, int partition_size, int max_partitions,
+                                int dtype, void* stream);
+
+/*
  * Measurement aid, not part of the decode step: reads `bytes` (a multiple of 16) at `buf` with
  * 16-byte loads (nontemporal if `nontemporal` != 0), each workgroup taking whole 64 KiB chunks,
  * and writes at most one word to `sink` (device memory, 4 bytes). Timing it gives the read rate

@@ -70,6 +70,8 @@ SIGNATURES = {
     "xs_step_graph_destroy": [_vp],
     "xs_kv_append_chunk": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp],
     "xs_paged_attn_prefill": [_vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp],
+    "xs_paged_attn_prefill_split": [_vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
+                                    _i, _i, _i, _vp],
     "xs_last_error": [],
     "xs_version": [],
 }
@@ -402,6 +404,42 @@ def xs_paged_attn_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
     _check("xs_paged_attn_prefill", load_library().xs_paged_attn_prefill(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(start_pos), _ptr(chunk_lens), float(scale),
         _ptr(out), B, Hq, Hkv, D, C, BS, block_tables.shape[1], NB, _dtype_code(q), _stream_handle(stream)))
+    return out
+
+
+def xs_paged_attn_prefill_split(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                block_tables: torch.Tensor, start_pos: torch.Tensor, chunk_lens: torch.Tensor,
+                                scale: float, partition_size: int, out: Optional[torch.Tensor] = None,
+                                part_o: Optional[torch.Tensor] = None, part_ml: Optional[torch.Tensor] = None,
+                                stream=None) -> torch.Tensor:
+    """xs_paged_attn_prefill with split-K over the key range (pieces of partition_size positions).
+    part_o [batch, Hq, chunk, NP, D] / part_ml [batch, Hq, chunk, NP, 2] fp32 scratch, NP =
+    ceil(max_blocks_per_seq * block_size / partition_size); allocated here when not given."""
+    _dev(q, k_cache, v_cache, block_tables, start_pos, chunk_lens, out, part_o, part_ml)
+    B, Hq, C, D = q.shape
+    NB, Hkv, BS, D2 = k_cache.shape
+    _need(D2 == D and v_cache.shape == k_cache.shape, "pool shapes do not match q")
+    _need(q.dtype == k_cache.dtype == v_cache.dtype, "q and the pools must have the same dtype")
+    _chunk_checks(B, block_tables, start_pos, chunk_lens)
+    MBPS = block_tables.shape[1]
+    _need(int(partition_size) > 0, "partition_size must be positive")
+    NP = num_partitions(MBPS * BS, int(partition_size))
+    if out is None:
+        out = torch.empty_like(q)
+    if part_o is None:
+        part_o = torch.empty((B, Hq, C, NP, D), dtype=torch.float32, device=q.device)
+    if part_ml is None:
+        part_ml = torch.empty((B, Hq, C, NP, 2), dtype=torch.float32, device=q.device)
+    _dev(out, part_o, part_ml)
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _need(part_o.dtype == torch.float32 and part_ml.dtype == torch.float32 and part_o.is_contiguous()
+          and part_ml.is_contiguous(), "partials must be contiguous fp32")
+    NP = part_o.shape[3] if part_o.dim() == 5 else NP
+    _need(part_o.shape == (B, Hq, C, NP, D) and part_ml.shape == (B, Hq, C, NP, 2), "partial shapes do not match")
+    _check("xs_paged_attn_prefill_split", load_library().xs_paged_attn_prefill_split(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(start_pos), _ptr(chunk_lens), float(scale),
+        _ptr(out), _ptr(part_o), _ptr(part_ml), B, Hq, Hkv, D, C, BS, MBPS, NB, int(partition_size), NP,
+        _dtype_code(q), _stream_handle(stream)))
     return out
 
 

@@ -516,12 +516,11 @@ XS_API int xs_kv_append_chunk(const void* k_src, const void* v_src, void* k_cach
                                                        static_cast<hipStream_t>(stream)));
 }
 
-XS_API int xs_paged_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
-                                 const int32_t* block_tables, const int32_t* start_pos, const int32_t* chunk_lens,
-                                 float scale, void* out, int batch, int num_q_heads, int num_kv_heads, int head_dim,
-                                 int chunk_size, int block_size, int max_blocks_per_seq, int num_blocks, int dtype,
-                                 void* stream) {
-  const char* who = "xs_paged_attn_prefill";
+static int prefill_common(const char* who, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* start_pos, const int32_t* chunk_lens,
+                          float scale, void* out, float* part_o, float* part_ml, int batch, int num_q_heads,
+                          int num_kv_heads, int head_dim, int chunk_size, int block_size, int max_blocks_per_seq,
+                          int num_blocks, int partition_size, int max_partitions, int dtype, void* stream) {
   int st = check_pool_args(who, batch, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, dtype);
   if (st != XS_OK) return st;
   if (dtype != XS_BF16) return fail(XS_EUNSUPPORTED, "%s: only XS_BF16 is implemented", who);
@@ -534,13 +533,28 @@ XS_API int xs_paged_attn_prefill(const void* q, const void* k_cache, const void*
   const int group = num_q_heads / num_kv_heads;
   if ((long long)chunk_size * group > 0x7fffffffLL - 64)
     return fail(XS_EINVAL, "%s: chunk_size * (num_q_heads / num_kv_heads) too large", who);
+  const bool split = partition_size != 0;
+  if (split) {
+    if (partition_size < 0 || partition_size % 64 != 0)
+      return fail(XS_EINVAL, "%s: partition_size = %d is not a positive multiple of 64", who, partition_size);
+    const long long need = ((long long)max_blocks_per_seq * block_size + partition_size - 1) / partition_size;
+    if (max_partitions < need)
+      return fail(XS_EINVAL, "%s: max_partitions = %d < %lld (max_blocks_per_seq * block_size / partition_size)",
+                  who, max_partitions, need);
+  }
   if (batch == 0 || chunk_size == 0) return ok();
-  const long long grid = (long long)batch * num_kv_heads * xs::prefill_row_blocks(chunk_size, group);
+  const long long grid =
+      (long long)batch * num_kv_heads * xs::prefill_row_blocks(chunk_size, group) * (split ? max_partitions : 1);
   if (grid > 0x7fffffffLL) return fail(XS_EINVAL, "%s: %lld workgroups exceed the launch limit", who, grid);
+  if (split && ((long long)batch * num_q_heads * chunk_size + 3) / 2 > 0x7fffffffLL)
+    return fail(XS_EINVAL, "%s: batch * num_q_heads * chunk_size too large", who);
   if (!q || !k_cache || !v_cache || !block_tables || !start_pos || !chunk_lens || !out)
     return fail(XS_EINVAL, "%s: a required pointer is NULL", who);
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return fail(XS_EINVAL, "%s: q, k_cache, v_cache and out must be 16-byte aligned", who);
+  if (split && (!part_o || !part_ml)) return fail(XS_EINVAL, "%s: part_o and part_ml are required", who);
+  if (split && (!aligned16(part_o) || reinterpret_cast<uintptr_t>(part_ml) % 8 != 0))
+    return fail(XS_EINVAL, "%s: part_o must be 16-byte and part_ml 8-byte aligned", who);
   xs::PrefillArgs a;
   a.q = q;
   a.k_cache = k_cache;
@@ -558,6 +572,35 @@ XS_API int xs_paged_attn_prefill(const void* q, const void* k_cache, const void*
   a.block_size = block_size;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
+  if (split) {
+    a.part_o = part_o;
+    a.part_ml = part_ml;
+    a.partition_size = partition_size;
+    a.max_partitions = max_partitions;
+  }
   (void)hipGetLastError();
   return launch_status(who, xs::launch_paged_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+XS_API int xs_paged_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* start_pos, const int32_t* chunk_lens,
+                                 float scale, void* out, int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                 int chunk_size, int block_size, int max_blocks_per_seq, int num_blocks, int dtype,
+                                 void* stream) {
+  return prefill_common("xs_paged_attn_prefill", q, k_cache, v_cache, block_tables, start_pos, chunk_lens, scale,
+                        out, nullptr, nullptr, batch, num_q_heads, num_kv_heads, head_dim, chunk_size, block_size,
+                        max_blocks_per_seq, num_blocks, 0, 0, dtype, stream);
+}
+
+XS_API int xs_paged_attn_prefill_split(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, const int32_t* start_pos,
+                                       const int32_t* chunk_lens, float scale, void* out, float* part_o,
+                                       float* part_ml, int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                       int chunk_size, int block_size, int max_blocks_per_seq, int num_blocks,
+                                       int partition_size, int max_partitions, int dtype, void* stream) {
+  const char* who = "xs_paged_attn_prefill_split";
+  if (partition_size == 0) return fail(XS_EINVAL, "%s: partition_size = 0 (use xs_paged_attn_prefill)", who);
+  return prefill_common(who, q, k_cache, v_cache, block_tables, start_pos, chunk_lens, scale, out, part_o, part_ml,
+                        batch, num_q_heads, num_kv_heads, head_dim, chunk_size, block_size, max_blocks_per_seq,
+                        num_blocks, partition_size, max_partitions, dtype, stream);
 }

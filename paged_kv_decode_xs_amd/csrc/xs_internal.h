@@ -125,8 +125,13 @@ struct PrefillArgs {
   float scale;
   void* out;
   int batch, num_q_heads, num_kv_heads, head_dim, chunk, block_size, max_blocks_per_seq, num_blocks;
+  // Split-K over the key range (partition_size 0: none): per-row partials of each piece.
+  float* part_o = nullptr;   // [B, Hq, C, max_partitions, D]
+  float* part_ml = nullptr;  // [B, Hq, C, max_partitions, 2]
+  int partition_size = 0;    // keys per piece, a multiple of 64
+  int max_partitions = 0;
 };
-// Workgroups per (sequence, kv head) of the prefill attention: chunk * group rows, 64 per group.
+// Row blocks per (sequence, kv head) of the prefill attention: chunk * group rows, 256 per block.
 int prefill_row_blocks(int chunk, int group);
 hipError_t launch_paged_prefill(const PrefillArgs& a, hipStream_t stream);
 

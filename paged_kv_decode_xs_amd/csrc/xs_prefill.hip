@@ -77,8 +77,12 @@ struct PrefillParams {
   const int32_t* start_pos;
   const int32_t* chunk_lens;
   uint4* out;
+  float* part_o;    // split only: [B, Hq, C, NP, D] f32, each row's output over one piece of keys
+  float2* part_ml;  // split only: [B, Hq, C, NP] (m, l) of those pieces (m in scaled log2 units)
   float scale_log2e;
   int batch, num_q_heads, num_kv_heads, group, chunk, row_blocks, bs_log2, max_blocks_per_seq, num_blocks;
+  int part_tiles;      // key tiles per piece (0: each workgroup takes its whole key range)
+  int max_partitions;  // NP
 };
 
 typedef float __attribute__((ext_vector_type(16))) float16_t;
@@ -143,14 +147,20 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
   const int n = lane & 31, hl = lane >> 5;  // score column (row of the chunk) and lane half
   const int j = lane >> 4, c = lane & 15;   // loader coordinates
 
-  // Workgroup -> (row block, sequence, kv head); the last row blocks (most keys) go first, and
-  // the workgroups of one (sequence, kv head) share blockIdx.x mod 8 (one XCD's L2) when the
-  // number of pairs is a multiple of 8.
-  const int pairs = prm.batch * prm.num_kv_heads;
-  const int rb = prm.row_blocks - 1 - (int)(blockIdx.x / (unsigned)pairs);
-  const int pair = (int)(blockIdx.x % (unsigned)pairs);
-  const int g = pair % prm.num_kv_heads;
-  const int b = pair / prm.num_kv_heads;
+  // Workgroup -> (piece, sequence, row block, kv head), kv head fastest, then row block (the last
+  // ones, with the most keys, first), sequence, piece. The device hands workgroup i to XCD i % 8,
+  // and within an XCD deals consecutive workgroups to its shader engines in turn, from one
+  // in-order queue that waits whenever the next workgroup's engine is full. With this order the
+  // engines of an XCD take row blocks of every sequence and piece alike (similar work, no engine
+  // holding up the queue), and the workgroups of one kv head share an XCD's L2 when the number of
+  // kv heads is a multiple of 8.
+  const int Hkv_ = prm.num_kv_heads;
+  const int g = (int)(blockIdx.x % (unsigned)Hkv_);
+  const int r1 = (int)(blockIdx.x / (unsigned)Hkv_);
+  const int rb = prm.row_blocks - 1 - r1 % prm.row_blocks;
+  const int r2 = r1 / prm.row_blocks;
+  const int b = r2 % prm.batch;
+  const int piece = r2 / prm.batch;
   const int G = prm.group;
   const int C = prm.chunk;
   const int BS = 1 << prm.bs_log2;
@@ -181,13 +191,20 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
   const int ntiles = i_hi_wg >= rho0_wg / G ? (s0 + i_hi_wg) / kTileTokens + 1 : 0;
   const int wave_tiles = wave_active ? (s0 + i_hi_wave) / kTileTokens + 1 : 0;
   const int kmax = s0 + i_hi_wg;  // last key position any row of the workgroup reads
+  // Split-K: this workgroup takes key tiles [t_lo, t_hi) of its row block. Pieces past the row
+  // block's keys leave at once; piece 0 always runs (it writes the zero rows).
+  const int PT = prm.part_tiles;
+  const int npieces = PT > 0 ? (ntiles + PT - 1) / PT : 1;
+  if (piece > 0 && piece >= npieces) return;
+  const int t_lo = PT > 0 ? piece * PT : 0;
+  const int t_hi = PT > 0 ? min(t_lo + PT, ntiles) : ntiles;
 
   float16_t acc[MD];
 #pragma unroll
   for (int md = 0; md < MD; ++md) acc[md] = float16_t{};
   float m_run = -INFINITY, l_part = 0.f;
 
-  if (ntiles > 0) {
+  if (t_hi > t_lo) {
     const int32_t* bt = prm.block_tables + (size_t)b * prm.max_blocks_per_seq;
     const int Hkv = prm.num_kv_heads;
     auto block_ok = [&](int blk) { return blk >= 0 && blk < prm.num_blocks; };
@@ -375,18 +392,18 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
     };
 
     TileRegs ra, rb;
-    int ida = tile_ids(0), idb;
-    load_tile(0, ida, ra);
-    store_tile(0, ra);
+    int ida = tile_ids(t_lo), idb;
+    load_tile(t_lo, ida, ra);
+    store_tile(t_lo & 1, ra);
     vbits = ra.vbits;
-    // Same order of loads as in a step: the ids of tile 2 before the loads of tile 1.
-    idb = tile_ids(1);
-    ida = tile_ids(2);
-    load_tile(1, idb, ra);
+    // Same order of loads as in a step: the ids of tile t_lo+2 before the loads of tile t_lo+1.
+    idb = tile_ids(t_lo + 1);
+    ida = tile_ids(t_lo + 2);
+    load_tile(t_lo + 1, idb, ra);
     __syncthreads();
-    for (int it = 0; it < ntiles; it += 2) {
+    for (int it = t_lo; it < t_hi; it += 2) {
       step(it, ra, rb, ida, idb);
-      if (it + 1 >= ntiles) break;
+      if (it + 1 >= t_hi) break;
       step(it + 1, rb, ra, idb, ida);
     }
   }
@@ -396,6 +413,23 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
   if (!row_exists) return;
   const float inv = row_valid && l_tot > 0.f ? 1.f / l_tot : 0.f;
   // acc[md][r] is O[row n][32md + 8(r/4) + 4hl + r%4]: four runs of 4 values per d block.
+  if (npieces > 1 && row_valid) {
+    // A piece of a split row block: this row's output over the piece's keys, and its (m, l)
+    // (m = -inf, l = 0 and a zero output for a row with no keys in the piece).
+    const size_t prow = out_row * prm.max_partitions + piece;
+    float4* po = reinterpret_cast<float4*>(prm.part_o + prow * D);
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float* o = reinterpret_cast<const float*>(&acc[md]) + 4 * q4;
+        po[8 * md + 2 * q4 + hl] = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+      }
+    }
+    if (hl == 0) prm.part_ml[prow] = make_float2(m_run, l_tot);
+    return;
+  }
+  if (piece > 0) return;  // rows past chunk_lens get their zeros from piece 0
   uint2* orow = reinterpret_cast<uint2*>(prm.out + out_row * ND);
 #pragma unroll
   for (int md = 0; md < MD; ++md) {
@@ -407,10 +441,79 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
   }
 }
 
+// Split-K merge of the rows of split row blocks (the others were written by the attention
+// kernel): 32 lanes per row, four consecutive d each. Row (b, h, i) combines the pieces that hold
+// keys it sees (pieces 0 .. pos / (64 PT)): M = max_j m_j, w_j = l_j 2^(m_j - M),
+// out = sum_j w_j o_j / sum_j w_j, taken four pieces at a time (their loads in flight together)
+// with a running maximum.
+constexpr int kMergeThreads = 256;
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillParams prm) {
+  constexpr int LPR = D / 4;                  // lanes per row
+  constexpr int RPB = kMergeThreads / LPR;  // rows per workgroup
+  const int sub = threadIdx.x % LPR;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;  // (b * Hq + h) * C + i
+  const int C = prm.chunk, G = prm.group;
+  if (row >= (long long)prm.batch * prm.num_q_heads * C) return;
+  const int i = (int)(row % C);
+  const int h = (int)((row / C) % prm.num_q_heads);
+  const int b = (int)(row / ((long long)C * prm.num_q_heads));
+  const int BS = 1 << prm.bs_log2;
+  const int s0 = prm.start_pos[b], nlen = prm.chunk_lens[b];
+  if (s0 < 0 || nlen < 0 || nlen > C || (long long)s0 + nlen > (long long)prm.max_blocks_per_seq * BS) return;
+  if (i >= nlen) return;
+  // The row's row block and whether it was split (the same arithmetic as the attention kernel).
+  const int rb = (i * G + h % G) / kRowsPerGroup;
+  const int i_hi_wg = min((min((rb + 1) * kRowsPerGroup, C * G) - 1) / G, nlen - 1);
+  const int ntiles = (s0 + i_hi_wg) / kTileTokens + 1;
+  const int PT = prm.part_tiles;
+  if ((ntiles + PT - 1) / PT <= 1) return;
+  const int nrow = (s0 + i) / (kTileTokens * PT) + 1;  // pieces holding keys 0 .. s0 + i
+  const size_t prow0 = (size_t)row * prm.max_partitions;
+  float M = -INFINITY, wsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j0 = 0; j0 < nrow; j0 += 4) {
+    float2 ml[4];
+    float4 o[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool in = j0 + u < nrow;
+      const size_t pr = prow0 + (in ? j0 + u : 0);
+      ml[u] = prm.part_ml[pr];
+      o[u] = reinterpret_cast<const float4*>(prm.part_o + pr * D)[sub];
+      if (!in) ml[u] = make_float2(-INFINITY, 0.f);
+    }
+    float Mn = M;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) Mn = fmaxf(Mn, ml[u].x);
+    if (Mn == -INFINITY) continue;  // no keys yet
+    const float f = fast_exp2(M - Mn);  // 0 while M is still -inf
+    wsum *= f;
+    acc = make_float4(acc.x * f, acc.y * f, acc.z * f, acc.w * f);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float w = ml[u].y * fast_exp2(ml[u].x - Mn);  // 0 for a piece with none of the row's keys
+      wsum += w;
+      acc = make_float4(fmaf(w, o[u].x, acc.x), fmaf(w, o[u].y, acc.y), fmaf(w, o[u].z, acc.z), fmaf(w, o[u].w, acc.w));
+    }
+    M = Mn;
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  reinterpret_cast<uint2*>(prm.out)[(size_t)row * (D / 4) + sub] =
+      make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
+}
+
 template <int D>
 hipError_t launch_prefill_d(const PrefillParams& p, hipStream_t stream) {
-  const long long grid = (long long)p.batch * p.num_kv_heads * p.row_blocks;
+  const long long pieces = p.part_tiles > 0 ? p.max_partitions : 1;
+  const long long grid = (long long)p.batch * p.num_kv_heads * p.row_blocks * pieces;
   hipLaunchKernelGGL(paged_prefill_kernel<D>, dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, p);
+  if (p.part_tiles > 0) {
+    const long long rows = (long long)p.batch * p.num_q_heads * p.chunk;
+    constexpr int rpb = kMergeThreads / (D / 4);
+    hipLaunchKernelGGL(prefill_merge_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(kMergeThreads), 0,
+                       stream, p);
+  }
   return hipGetLastError();
 }
 
@@ -442,6 +545,10 @@ hipError_t launch_paged_prefill(const PrefillArgs& a, hipStream_t stream) {
   p.start_pos = a.start_pos;
   p.chunk_lens = a.chunk_lens;
   p.out = static_cast<uint4*>(a.out);
+  p.part_o = a.part_o;
+  p.part_ml = reinterpret_cast<float2*>(a.part_ml);
+  p.part_tiles = a.partition_size / kTileTokens;
+  p.max_partitions = a.max_partitions;
   p.scale_log2e = a.scale * kLog2e;
   p.batch = a.batch;
   p.num_q_heads = a.num_q_heads;

@@ -338,6 +338,39 @@ def test_prefill_rejects(kw, status, needle):
     assert needle in xb.xs_last_error()
 
 
+def _prefill_split(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sp=FAKE, cl=FAKE, scale=0.125, out=FAKE, po=FAKE, pml=FAKE, batch=2,
+             hq=8, hkv=2, d=128, c=16, bs=16, mbps=4, nb=16, p=64, np_=1, dt=B)
+    a.update(kw)
+    return xb.load_library().xs_paged_attn_prefill_split(
+        a["q"], a["kc"], a["vc"], a["bt"], a["sp"], a["cl"], a["scale"], a["out"], a["po"], a["pml"], a["batch"],
+        a["hq"], a["hkv"], a["d"], a["c"], a["bs"], a["mbps"], a["nb"], a["p"], a["np_"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(p=0), 1, "partition_size = 0"),
+    (dict(p=96), 1, "multiple of 64"),
+    (dict(p=-64), 1, "multiple of 64"),
+    (dict(p=32, np_=2), 1, "multiple of 64"),
+    (dict(mbps=8), 1, "max_partitions = 1 < 2"),
+    (dict(po=None), 1, "part_o and part_ml"),
+    (dict(pml=None), 1, "part_o and part_ml"),
+    (dict(po=FAKE + 8), 1, "aligned"),
+    (dict(pml=FAKE + 4), 1, "aligned"),
+    (dict(dt=F), 2, "XS_BF16"),
+    (dict(out=None), 1, "NULL"),
+    (dict(batch=1 << 16, hkv=64, hq=64, c=1 << 12, np_=1 << 10, mbps=1 << 12, p=64), 1, "launch limit"),
+])
+def test_prefill_split_rejects(kw, status, needle):
+    assert _prefill_split(**kw) == status
+    assert needle in xb.xs_last_error()
+
+
+def test_prefill_split_empty_is_a_noop():
+    assert _prefill_split(batch=0, q=None, out=None, po=None, pml=None) == 0
+    assert _prefill_split(c=0, q=None, out=None, po=None, pml=None) == 0
+
+
 def test_prefill_empty_is_a_noop():
     assert _prefill(batch=0, q=None, out=None) == 0
     assert _prefill(c=0, q=None, out=None) == 0

@@ -10,6 +10,9 @@ that start at 0 or deep into a cached prefix, empty chunks and sequences outside
 The Qwen3-8B 512-token chunk workload (the timed one) is checked in full for the append and on
 sampled rows for the attention: a run of rows [a, a+k) of the chunk is what the oracle gives for
 a chunk that starts at start_pos + a (the chunking invariance pinned on the CPU).
+The split-K entry point (xs_paged_attn_prefill_split) is held to the same bar with partition
+sizes of 64 and 128 keys, so the small shapes already split into several pieces and rows see
+pieces with and without keys of their own.
 """
 
 import numpy as np
@@ -46,9 +49,16 @@ def _to_dev(case):
     }
 
 
-def _run(dev, scale):
+def _attend(dev, scale, split=None):
+    if split:
+        return xs.xs_paged_attn_prefill_split(dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"], dev["sp"], dev["cl"],
+                                              scale, split)
+    return xs.xs_paged_attn_prefill(dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"], dev["sp"], dev["cl"], scale)
+
+
+def _run(dev, scale, split=None):
     xs.xs_kv_append_chunk(dev["k_src"], dev["v_src"], dev["k_cache"], dev["v_cache"], dev["bt"], dev["sp"], dev["cl"])
-    out = xs.xs_paged_attn_prefill(dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"], dev["sp"], dev["cl"], scale)
+    out = _attend(dev, scale, split)
     torch.cuda.synchronize()
     return out
 
@@ -59,24 +69,24 @@ def _check_pools(dev, kp, vp):
         assert np.array_equal(got.view(np.uint8), exp.view(np.uint8)), f"{name} differs after the chunk append"
 
 
-def _full_check(w, label):
+def _full_check(w, label, split=None):
     log(f"[gpu] prefill {label}: Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim} BS={w.block_size} "
-        f"C={w.chunk} start={w.start_pos} n={w.chunk_lens}")
+        f"C={w.chunk} start={w.start_pos} n={w.chunk_lens} split={split}")
     case = make_prefill_case(w)
     kp, vp = oracle.kv_append_chunk(case.k_cache, case.v_cache, case.k_src, case.v_src, case.block_tables,
                                     case.start_pos, case.chunk_lens, w.block_size)
     exp = oracle.paged_prefill_attention(case.q, kp, vp, case.block_tables, case.start_pos, case.chunk_lens, w.scale,
                                          w.block_size, "bf16")
     dev = _to_dev(case)
-    out = _run(dev, w.scale)
+    out = _run(dev, w.scale, split)
     _check_pools(dev, kp, vp)
     got = as_f64(out)
     atol, rtol = TOL["bf16"]
-    err = assert_close(got, exp, atol, rtol, f"prefill {label}")
+    err = assert_close(got, exp, atol, rtol, f"prefill {label} split={split}")
     for b, n in enumerate(case.chunk_lens.tolist()):
         assert not got[b, :, n:].any(), f"rows past chunk_lens[{b}] = {n} are not zero"
     # Deterministic: a second run on the same inputs gives the same bits.
-    out2 = xs.xs_paged_attn_prefill(dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"], dev["sp"], dev["cl"], w.scale)
+    out2 = _attend(dev, w.scale, split)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
     return err
@@ -95,39 +105,52 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"Hq{s[0]}_Hkv{s[1]}_D{s[2]}_BS{s[3]}_C{s[4]}")
-def test_prefill_matches_oracle(shape):
+def _shape_workload(shape):
     Hq, Hkv, D, BS, C, sp, cl = shape
     mbps = -(-max(s + n for s, n in zip(sp, cl)) // BS) + 2
-    w = PrefillWorkload(name="t", description="", dtype="bf16", num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
-                        block_size=BS, chunk=C, start_pos=sp, chunk_lens=cl, max_blocks_per_seq=mbps,
-                        seed=hash(shape) % 1000)
-    _full_check(w, f"Hq{Hq} Hkv{Hkv} D{D} BS{BS} C{C}")
+    return PrefillWorkload(name="t", description="", dtype="bf16", num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                           block_size=BS, chunk=C, start_pos=sp, chunk_lens=cl, max_blocks_per_seq=mbps,
+                           seed=hash(shape) % 1000)
 
 
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"Hq{s[0]}_Hkv{s[1]}_D{s[2]}_BS{s[3]}_C{s[4]}")
+def test_prefill_matches_oracle(shape):
+    Hq, Hkv, D, BS, C = shape[:5]
+    _full_check(_shape_workload(shape), f"Hq{Hq} Hkv{Hkv} D{D} BS{BS} C{C}")
+
+
+@pytest.mark.parametrize("split", [64, 128])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"Hq{s[0]}_Hkv{s[1]}_D{s[2]}_BS{s[3]}_C{s[4]}")
+def test_prefill_split_matches_oracle(shape, split):
+    Hq, Hkv, D, BS, C = shape[:5]
+    _full_check(_shape_workload(shape), f"Hq{Hq} Hkv{Hkv} D{D} BS{BS} C{C}", split)
+
+
+@pytest.mark.parametrize("split", [None, 64])
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
-def test_prefill_scale_sign_and_zero(scale):
+def test_prefill_scale_sign_and_zero(scale, split):
     # A negative scale (q negated inside the kernel), scale 0 (uniform weights over the visible
     # keys) and a large one (sharp softmax, many rescales).
     w = PrefillWorkload(name="t", description="", dtype="bf16", num_q_heads=8, num_kv_heads=2, head_dim=128,
                         block_size=16, chunk=40, start_pos=(0, 70), chunk_lens=(40, 29), max_blocks_per_seq=8,
                         seed=21)
-    log(f"[gpu] prefill scale={scale}")
+    log(f"[gpu] prefill scale={scale} split={split}")
     case = make_prefill_case(w)
     kp, vp = oracle.kv_append_chunk(case.k_cache, case.v_cache, case.k_src, case.v_src, case.block_tables,
                                     case.start_pos, case.chunk_lens, w.block_size)
     exp = oracle.paged_prefill_attention(case.q, kp, vp, case.block_tables, case.start_pos, case.chunk_lens, scale,
                                          w.block_size, "bf16")
     dev = _to_dev(case)
-    out = _run(dev, scale)
-    assert_close(as_f64(out), exp, *TOL["bf16"], f"prefill scale={scale}")
+    out = _run(dev, scale, split)
+    assert_close(as_f64(out), exp, *TOL["bf16"], f"prefill scale={scale} split={split}")
 
 
-def test_invalid_sequences_get_zero_rows_and_no_append():
+@pytest.mark.parametrize("split", [None, 64])
+def test_invalid_sequences_get_zero_rows_and_no_append(split):
     w = PrefillWorkload(name="t", description="", dtype="bf16", num_q_heads=8, num_kv_heads=2, head_dim=64,
                         block_size=16, chunk=20, start_pos=(0, 10, 5, 16), chunk_lens=(20, 20, 7, 12),
                         max_blocks_per_seq=3, seed=11)
-    log("[gpu] prefill invalid ranges")
+    log(f"[gpu] prefill invalid ranges split={split}")
     case = make_prefill_case(w)
     dev = _to_dev(case)
     # Sequence 1: start_pos < 0. Sequence 2: chunk_lens > chunk. Sequence 3: start + n > 48 slots.
@@ -135,7 +158,7 @@ def test_invalid_sequences_get_zero_rows_and_no_append():
     cl = torch.tensor([20, 20, 21, 12], dtype=torch.int32)
     dev["sp"].copy_(sp)
     dev["cl"].copy_(cl)
-    out = _run(dev, w.scale)
+    out = _run(dev, w.scale, split)
     valid = np.array([True, False, False, False])
     kp, vp = oracle.kv_append_chunk(case.k_cache, case.v_cache, case.k_src[valid], case.v_src[valid],
                                     case.block_tables[valid], case.start_pos[valid], case.chunk_lens[valid],
@@ -168,14 +191,17 @@ def test_append_chunk_f32_bit_exact():
     assert np.array_equal(vc.cpu().numpy().view(np.uint32), ev.view(np.uint32))
 
 
-def test_qwen3_prefill_workload_sampled_rows():
-    w = PREFILL_WORKLOADS["qwen3_8b_prefill_c512"]
-    log(f"[gpu] prefill {w.name} (full size, sampled rows)")
+@pytest.mark.parametrize("name,split", [("qwen3_8b_prefill_c512", None), ("qwen3_8b_prefill_c512", 512),
+                                        ("qwen3_8b_prefill_c512", 1024), ("qwen3_8b_prefill_long16k", None),
+                                        ("qwen3_8b_prefill_long16k", 2048), ("qwen3_8b_prefill_long16k", 1024)])
+def test_qwen3_prefill_workload_sampled_rows(name, split):
+    w = PREFILL_WORKLOADS[name]
+    log(f"[gpu] prefill {w.name} (full size, sampled rows) split={split}")
     case = make_prefill_case(w)
     kp, vp = oracle.kv_append_chunk(case.k_cache, case.v_cache, case.k_src, case.v_src, case.block_tables,
                                     case.start_pos, case.chunk_lens, w.block_size)
     dev = _to_dev(case)
-    out = _run(dev, w.scale)
+    out = _run(dev, w.scale, split)
     _check_pools(dev, kp, vp)
     got = as_f64(out)
     assert np.isfinite(got).all()

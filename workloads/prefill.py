@@ -105,6 +105,14 @@ PREFILL_WORKLOADS: Dict[str, PrefillWorkload] = {
             dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, chunk=512,
             start_pos=(0, 1024, 2048, 3584), chunk_lens=(512, 512, 512, 512), max_blocks_per_seq=256, seed=6,
         ),
+        PrefillWorkload(
+            name="qwen3_8b_prefill_long16k",
+            description="Qwen3-8B shape, bf16 chunked prefill deep into one long context: 1 sequence, a "
+            "512-token chunk after 15872 cached tokens (16384 after the step), 32 q / 8 KV heads, head_dim "
+            "128, block_size 16 (64 row blocks: the split-K case)",
+            dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, chunk=512,
+            start_pos=(15872,), chunk_lens=(512,), max_blocks_per_seq=1024, seed=7,
+        ),
     ]
 }
 
