@@ -418,7 +418,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 PREFILL_SPLITS = {"qwen3_8b_prefill_c512": (1024, 2048), "qwen3_8b_prefill_long16k": (1024, 2048, 4096)}
 
 
-def prefill_row(name: str = "qwen3_8b_prefill_c512", reps: int = 20) -> dict:
+def prefill_row(name: str = "qwen3_8b_prefill_c512", reps: int = 20, partitions=None) -> dict:
     """Chunked prefill on the Qwen3-8B shape: the multi-token append and the causal attention of
     the chunk, each timed alone (HIP events on the launch stream, median of `reps`: around one
     attention call, around 20 back-to-back append launches). The attention is timed whole
@@ -426,7 +426,8 @@ def prefill_row(name: str = "qwen3_8b_prefill_c512", reps: int = 20) -> dict:
     attention kernel and the merge kernel) at the partition sizes of PREFILL_SPLITS; the roofline
     object is the fastest of them. It is a dense contraction on the matrix cores: algorithmic flops
     (4 * head_dim per (query head, chunk row, visible key)) over its time, against the bf16 dense
-    MFMA peak. The append moves bytes: read + write of every chunk row, against HBM peak."""
+    MFMA peak. The append moves bytes: read + write of every chunk row, against HBM peak.
+    `partitions` (a list, 0 = the whole call) restricts the timed paths, for profiling one."""
     import torch
 
     import paged_kv_decode_xs_amd as xs
@@ -465,9 +466,13 @@ def prefill_row(name: str = "qwen3_8b_prefill_c512", reps: int = 20) -> dict:
         for _ in range(20):
             xs.xs_kv_append_chunk(ks, vs, kc, vc, bt, sp, cl, stream=stream)
     append_ms = med(append20) / 20
-    by_p = {0: med(lambda: xs.xs_paged_attn_prefill(q, kc, vc, bt, sp, cl, w.scale, out=out, stream=stream))}
-    finite = bool(torch.isfinite(out.float()).all().item())
-    for P in PREFILL_SPLITS.get(name, ()):
+    paths = [0, *PREFILL_SPLITS.get(name, ())] if partitions is None else list(partitions)
+    by_p = {}
+    finite = True
+    if 0 in paths:
+        by_p[0] = med(lambda: xs.xs_paged_attn_prefill(q, kc, vc, bt, sp, cl, w.scale, out=out, stream=stream))
+        finite = bool(torch.isfinite(out.float()).all().item())
+    for P in (p for p in paths if p):
         NP = xs.num_partitions(bt.shape[1] * kc.shape[2], P)
         po = torch.empty((*q.shape[:3], NP, q.shape[3]), dtype=torch.float32, device="cuda")
         pml = torch.empty((*q.shape[:3], NP, 2), dtype=torch.float32, device="cuda")
@@ -551,7 +556,11 @@ def main() -> int:
                     help="after the timed work, copy a 1 GiB buffer 5 times with torch (a plain copy kernel of "
                          "known size, to calibrate rocprofv3's FETCH_SIZE/WRITE_SIZE)")
     ap.add_argument("--prefill-only", action="store_true",
-                    help="time only the chunked-prefill row (append + attention) and print its JSON line")
+                    help="time only the chunked-prefill rows (append + attention) and print their JSON line")
+    ap.add_argument("--prefill-workload", default=None,
+                    help="with --prefill-only: just this prefill workload")
+    ap.add_argument("--prefill-partition", type=int, default=None,
+                    help="with --prefill-only: just this attention path (0 = whole, else the split-K partition size)")
     ap.add_argument("--no-fuse", action="store_true",
                     help="issue xs_kv_append and xs_paged_attn_decode separately instead of the fused call")
     args = ap.parse_args()
@@ -573,8 +582,10 @@ def main() -> int:
     xs.load_library()  # raises if libxs.so is missing: there is no fallback path
     if args.prefill_only:
         reps = max(args.steps, 5)
-        print(json.dumps({"chunked_prefill": prefill_row(reps=reps),
-                          "chunked_prefill_long": prefill_row("qwen3_8b_prefill_long16k", reps=reps)}), flush=True)
+        parts = None if args.prefill_partition is None else [args.prefill_partition]
+        rows = {"chunked_prefill": "qwen3_8b_prefill_c512", "chunked_prefill_long": "qwen3_8b_prefill_long16k"}
+        print(json.dumps({k: prefill_row(n, reps=reps, partitions=parts) for k, n in rows.items()
+                          if args.prefill_workload in (None, n)}), flush=True)
         return 0
 
     w = wl.WORKLOADS[args.workload]
