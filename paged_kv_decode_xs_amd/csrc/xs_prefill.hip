@@ -24,6 +24,10 @@
 // The next two tiles are loaded into registers while the current one is processed
 // (double-buffered LDS, one barrier per tile). Tokens past the causal limit of a row get score
 // -inf, and K/V of positions past the workgroup's last key or in a bad block are zero.
+// Split-K (partition size P > 0): a workgroup takes one piece of P key positions of its row
+// block; a row block with several pieces leaves each row's normalised output over the piece and
+// its (max, sum) in the caller's partials, and the merge kernel combines them per row with the
+// log-sum-exp identity (the same as the decode's partition merge).
 #include <math.h>
 
 #include "xs_internal.h"
