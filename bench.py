@@ -116,7 +116,9 @@ def _cpu_model() -> str:
 
 
 def cpu_baseline(case, gpu_out, budget_s: float):
-    """Time the fp64 oracle over whole sequences until the time budget is used; compare outputs."""
+    """Time the fp64 oracle over whole sequences until the time budget is used, and compare its
+    outputs with the GPU's. When that first pass covers the batch in under a third of the budget,
+    two more passes are timed and the median pass time is the one reported (median of 3)."""
     import oracle  # the oracle is test infrastructure; this leg is the only bench code that uses it
 
     threads = None
@@ -145,6 +147,16 @@ def cpu_baseline(case, gpu_out, budget_s: float):
         done += 1
         if elapsed >= budget_s:
             break
+    passes = [elapsed]
+    if done == w.batch and 3 * elapsed < budget_s:
+        for _ in range(2):
+            t0 = time.perf_counter()
+            for b in range(w.batch):
+                sl = slice(b, b + 1)
+                oracle.paged_decode_attention(case.q[sl], k_pool, v_pool, case.block_tables[sl], case.context_lens[sl],
+                                              w.scale, w.block_size, w.dtype)
+            passes.append(time.perf_counter() - t0)
+    elapsed = float(np.median(passes))
     return {
         "value": round(kv_bytes / elapsed / 1e9, 4),
         "unit": "GB/s",
@@ -152,8 +164,9 @@ def cpu_baseline(case, gpu_out, budget_s: float):
         "kind": "oracle",
         "sample": f"fp64 numpy oracle attention over the first {done} of {w.batch} sequences "
                   f"({int(case.context_lens[:done].sum())} tokens, {kv_bytes / 1e6:.1f} MB of K+V), "
-                  f"{elapsed:.2f} s; K+V bytes of the sample / oracle time",
+                  f"{elapsed:.2f} s (median of {len(passes)} timed passes); K+V bytes of the sample / oracle time",
         "seconds": round(elapsed, 3),
+        "passes_s": [round(t, 3) for t in passes],
         "cpu_model": _cpu_model(),
         "host_cpus": os.cpu_count(),
     }, {"sequences_checked": done, "max_abs_err": max_err, "out_of_tolerance": bad}
