@@ -352,6 +352,7 @@ DecodeParams make_params(const DecodeArgs& a, int heads_per_wave) {
   p.sinks = static_cast<const uint16_t*>(a.sinks);
   p.window = a.window;
   p.batch = a.batch;
+  p.ncu = device_cu_count();
   p.out = a.out;
   p.part_o = a.part_o;
   p.part_m = a.part_m;

@@ -235,13 +235,22 @@ __device__ __forceinline__ void seq_partitions(const DecodeParams& prm, int b, i
   npartial = nblk % prm.part_blocks != 0 && nblk / prm.part_blocks < prm.max_partitions ? 1 : 0;
 }
 
-// The k-th existing split item (full partitions first, sequence-major, then the partial ones):
-// sets b, p and seg (kv head * chunks + chunk); b = -1 when there are fewer than k + 1 items.
+// Split items in the order that evens out the work per CU: full partitions first
+// (sequence-major, all the same size), then the partial last partitions by decreasing size (ties
+// by sequence; batches of more than 64 sequences keep sequence order). Workgroup k takes the item
+// whose rank is k with every second round of ncu consecutive ids reversed: with the whole grid
+// resident, ids k and k + ncu share a CU (the device deals workgroups to its CUs in turn), so a CU
+// that gets one of the larger partial items in one round gets one of the smaller ones in the
+// next. Sets b, p and seg (kv head * chunks + chunk); b = -1 when the rank is past the last item.
 template <int BS>
 __device__ __forceinline__ void dense_item(const DecodeParams& prm, int k, int& b, int& p, int& seg) {
   const int lane = threadIdx.x & 63;
   const int batch = prm.batch;
   const int segs = prm.num_kv_heads * prm.chunks;
+  const int ncu = max(prm.ncu, 1);
+  const int rnd = k / ncu, col = k - rnd * ncu;
+  // Only whole rounds are reversed, so every rank below the grid size keeps exactly one id.
+  if ((rnd & 1) && (long long)(rnd + 1) * ncu <= (long long)gridDim.x) k = rnd * ncu + (ncu - 1 - col);
   int F = 0;
   for (int b0 = 0; b0 < batch; b0 += 64) {
     int nf = 0, np1 = 0;
@@ -255,26 +264,44 @@ __device__ __forceinline__ void dense_item(const DecodeParams& prm, int k, int& 
   b = -1;
   p = 0;
   seg = 0;
-  int base = 0;
-  for (int b0 = 0; b0 < batch && b < 0; b0 += 64) {
+  if (!full && batch <= 64) {
+    // Rank of this lane's sequence among those with a partial partition, by decreasing size.
     int nf = 0, np1 = 0;
-    if (b0 + lane < batch) seq_partitions<BS>(prm, b0 + lane, nf, np1);
-    const int own = (full ? nf : np1) * segs;
-    int incl = own;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += y;
-    }
-    const unsigned long long hit = __ballot(b0 + lane < batch && base + incl > k);
+    if (lane < batch) seq_partitions<BS>(prm, lane, nf, np1);
+    const int L = lane < batch ? min(prm.context_lens[lane], prm.max_blocks_per_seq * BS) : 0;
+    const int nblk = L > 0 ? (L + BS - 1) / BS : 0;
+    const int key = np1 ? ((nblk - nf * prm.part_blocks) << 8) | (255 - lane) : -1;  // unique when >= 0
+    int rank = 0;
+    for (int jl = 0; jl < batch; ++jl) rank += __builtin_amdgcn_readlane(key, jl) > key ? 1 : 0;
+    const unsigned long long hit = __ballot(np1 && rank == k / segs);
     if (hit) {
       const int first = __builtin_ctzll(hit);
-      const int r = k - base - __shfl(incl - own, first, 64);
-      b = b0 + first;
-      p = full ? r / segs : __shfl(nf, first, 64);
-      seg = full ? r % segs : r;
-    } else {
-      base += __shfl(incl, 63, 64);
+      b = first;
+      p = __shfl(nf, first, 64);
+      seg = k % segs;
+    }
+  } else {
+    int base = 0;
+    for (int b0 = 0; b0 < batch && b < 0; b0 += 64) {
+      int nf = 0, np1 = 0;
+      if (b0 + lane < batch) seq_partitions<BS>(prm, b0 + lane, nf, np1);
+      const int own = (full ? nf : np1) * segs;
+      int incl = own;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      const unsigned long long hit = __ballot(b0 + lane < batch && base + incl > k);
+      if (hit) {
+        const int first = __builtin_ctzll(hit);
+        const int r = k - base - __shfl(incl - own, first, 64);
+        b = b0 + first;
+        p = full ? r / segs : __shfl(nf, first, 64);
+        seg = full ? r % segs : r;
+      } else {
+        base += __shfl(incl, 63, 64);
+      }
     }
   }
   b = __builtin_amdgcn_readfirstlane(b);

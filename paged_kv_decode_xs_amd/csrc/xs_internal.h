@@ -50,6 +50,7 @@ struct DecodeParams {
   const uint16_t* sinks;  // bf16 sink logit per query head, or null
   int window;             // 0: all positions
   int batch;
+  int ncu;                // compute units of the device (the split grid's work order)
 };
 
 DecodeParams make_params(const DecodeArgs& a, int heads_per_wave);
