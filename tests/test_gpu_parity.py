@@ -166,11 +166,14 @@ def test_fused_append_is_bitwise_the_two_calls(dtype, Hq, Hkv, D, BS, lens, P):
 
 
 def test_split_order_for_large_and_small_batches():
-    # The split grid maps workgroup ids onto the partitions that exist (dense order) for batches
-    # of up to 256 sequences and keeps partition-major ids above that; both orders must give the
-    # oracle's result, with partitions past a sequence's end and empty sequences mixed in.
+    # The split grid maps workgroup ids onto the partitions that exist for batches of up to 256
+    # sequences (full partitions first, then the partial ones, ranked by size for up to 64
+    # sequences, with every second whole round of CU-count ids reversed) and keeps
+    # partition-major ids above that. Every order must give the oracle's result, with partitions
+    # past a sequence's end, empty sequences, tied partial sizes and a last round that is not
+    # whole mixed in.
     rng = np.random.default_rng(31)
-    for B in (256, 300):
+    for B in (64, 65, 256, 300):
         lens = rng.integers(0, 400, B).tolist()
         lens[3] = 0
         lens[5] = 1
