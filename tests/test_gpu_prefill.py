@@ -10,7 +10,9 @@ that start at 0 or deep into a cached prefix, empty chunks and sequences outside
 The Qwen3-8B 512-token chunk workload (the timed one) is checked in full for the append and on
 sampled rows for the attention: a run of rows [a, a+k) of the chunk is what the oracle gives for
 a chunk that starts at start_pos + a (the chunking invariance pinned on the CPU).
-The split-K entry point (xs_paged_attn_prefill_split) is held to the same bar with partition
+The prefill kernel's rows also agree with the decode kernel's output for the same queries on the
+same pools (twice the bf16 bar: each is within it of the oracle). The split-K entry point
+(xs_paged_attn_prefill_split) is held to the same bar with partition
 sizes of 64 and 128 keys, so the small shapes already split into several pieces and rows see
 pieces with and without keys of their own.
 """
@@ -215,3 +217,39 @@ def test_qwen3_prefill_workload_sampled_rows(name, split):
                                                  case.start_pos[b:b + 1] + a, np.array([k], np.int32), w.scale,
                                                  w.block_size, "bf16")
             assert_close(got[b:b + 1, :, a:a + k], exp[:, :, :k], atol, rtol, f"{w.name} b={b} rows {a}..{a + k - 1}")
+
+
+@pytest.mark.parametrize("decode_split", [0, 64])
+def test_prefill_rows_agree_with_decode(decode_split):
+    # Row i of a chunk is a decode query at position start_pos + i: on the same pools, the prefill
+    # kernel's row and the decode kernel's output for that query (context length start_pos + i + 1)
+    # are the same attention, computed by two different kernels.
+    w = PrefillWorkload(name="t", description="", dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
+                        block_size=16, chunk=70, start_pos=(0, 130, 257), chunk_lens=(70, 64, 3),
+                        max_blocks_per_seq=24, seed=41)
+    log(f"[gpu] prefill rows vs decode (decode partition {decode_split})")
+    case = make_prefill_case(w)
+    dev = _to_dev(case)
+    out = _run(dev, w.scale)
+    B, Hq, D = w.batch, w.num_q_heads, w.head_dim
+    atol, rtol = TOL["bf16"]
+    for i in (0, 1, 2, 31, 63, 69):
+        rows = [b for b in range(B) if i < w.chunk_lens[b]]
+        q_i = dev["q"][:, :, i, :].contiguous()
+        lens = torch.tensor([w.start_pos[b] + min(i, w.chunk_lens[b] - 1) + 1 for b in range(B)], dtype=torch.int32,
+                            device="cuda")
+        dec = torch.empty((B, Hq, D), dtype=q_i.dtype, device="cuda")
+        if decode_split:
+            NP = xs.num_partitions(w.max_blocks_per_seq * w.block_size, decode_split)
+            po = torch.empty((B, Hq, NP, D), dtype=torch.float32, device="cuda")
+            pm = torch.empty((B, Hq, NP), dtype=torch.float32, device="cuda")
+            pl = torch.empty((B, Hq, NP), dtype=torch.float32, device="cuda")
+            xs.xs_paged_attn_decode(q_i, dev["k_cache"], dev["v_cache"], dev["bt"], lens, w.scale, part_o=po, part_m=pm,
+                                    part_l=pl, partition_size=decode_split)
+            xs.xs_paged_attn_reduce(po, pm, pl, lens, dec, decode_split)
+        else:
+            xs.xs_paged_attn_decode(q_i, dev["k_cache"], dev["v_cache"], dev["bt"], lens, w.scale, out=dec)
+        torch.cuda.synchronize()
+        got = as_f64(out)[rows, :, i]
+        ref = as_f64(dec)[rows]
+        assert_close(got, ref, 2 * atol, 2 * rtol, f"prefill row {i} vs decode")
