@@ -6,15 +6,18 @@
 * reduced shapes that span several blocks and partitions with ragged tails, every supported
   head_dim / block_size / dtype, GQA groups 1..16, L = 0 and L = 1;
 * invariants on the GPU: a block-table permutation gives bitwise the same output, as does a
-  second run; one key returns its V exactly.
+  second run; one key returns its V exactly;
+* block ids outside [0, num_blocks) inside a context are skipped (no access, no contribution),
+  unsplit, split and fused; the split item orders for small and large batches.
 """
 
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads as wl
-from tests.gpu_common import OracleResult, as_f64, check_case, log, run_step
+from tests.gpu_common import TOL, OracleResult, as_f64, assert_close, check_case, log, run_step
 from workloads.device import case_to_device
 
 pytestmark = pytest.mark.gpu
@@ -181,3 +184,33 @@ def test_split_order_for_large_and_small_batches():
         ref = OracleResult(case, 64)
         check_case(case, 64, ref, check_pools=False, label=f"split order B={B}")
         check_case(case, 64, ref, label=f"split order B={B} fused", fused=True)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("P", [0, 16, 32])
+def test_bad_block_ids_are_skipped(P, fused):
+    # Block ids outside [0, num_blocks) inside a context are skipped: sequence 0's table
+    # [b0, -1, b2, NB + 5] with L = 64 attends over the 32 tokens of b0 and b2 only, which is the
+    # oracle's result for the table [b0, b2] with L = 32 (decode attention does not depend on the
+    # order of its keys). The append into a bad block is skipped too; sequence 1 is unaffected.
+    case = _shape_case("bf16", 8, 2, 128, 16, [64, 40], seed=51)
+    w = case.workload
+    NB = case.num_blocks
+    bt = case.block_tables.copy()
+    b0, b2 = int(bt[0, 0]), int(bt[0, 2])
+    bad = bt.copy()
+    bad[0, 1] = -1
+    bad[0, 3] = NB + 5
+    log(f"[gpu] bad block ids: P={P} fused={fused} table0={bad[0, :4].tolist()}")
+    kp, vp = oracle.kv_append(case.k_cache, case.v_cache, case.k_new, case.v_new, bt, case.context_lens, w.block_size)
+    exp_bt = np.full_like(bt, -1)
+    exp_bt[0, :2] = [b0, b2]
+    exp_bt[1] = bt[1]
+    exp = oracle.paged_decode_attention(case.q, kp, vp, exp_bt, np.array([32, 40], np.int32), w.scale, w.block_size,
+                                        w.dtype)
+    dev = case_to_device(case)
+    dev["block_tables"].copy_(torch.from_numpy(bad))
+    step = run_step(dev, w.scale, P, 64 if P else None, fused=fused)
+    got = as_f64(step.out)
+    assert np.isfinite(got).all()
+    assert_close(got, exp, *TOL["bf16"], f"bad block ids P={P} fused={fused}")
