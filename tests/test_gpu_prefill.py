@@ -10,7 +10,9 @@ that start at 0 or deep into a cached prefix, empty chunks and sequences outside
 The Qwen3-8B 512-token chunk workload (the timed one) is checked in full for the append and on
 sampled rows for the attention: a run of rows [a, a+k) of the chunk is what the oracle gives for
 a chunk that starts at start_pos + a (the chunking invariance pinned on the CPU).
-The prefill kernel's rows also agree with the decode kernel's output for the same queries on the
+A block id outside [0, num_blocks) in the cached prefix is skipped (checked against the decode
+oracle over the table without it). The prefill kernel's rows also agree with the decode kernel's
+output for the same queries on the
 same pools (twice the bf16 bar: each is within it of the oracle). The split-K entry point
 (xs_paged_attn_prefill_split) is held to the same bar with partition
 sizes of 64 and 128 keys, so the small shapes already split into several pieces and rows see
@@ -253,3 +255,32 @@ def test_prefill_rows_agree_with_decode(decode_split):
         got = as_f64(out)[rows, :, i]
         ref = as_f64(dec)[rows]
         assert_close(got, ref, 2 * atol, 2 * rtol, f"prefill row {i} vs decode")
+
+
+@pytest.mark.parametrize("split", [None, 64])
+def test_prefill_skips_bad_block_ids(split):
+    # A block id outside [0, num_blocks) inside the cached prefix is skipped: with the table
+    # [b0, -1, b2, b3, b4] (block_size 16) and the chunk at positions 32..71, row i (position p)
+    # sees positions 0..15 and 32..p, which is a decode query over the table [b0, b2, b3, b4]
+    # with context length p + 1 - 16 (the decode oracle, pinned on the CPU).
+    w = PrefillWorkload(name="t", description="", dtype="bf16", num_q_heads=8, num_kv_heads=2, head_dim=128,
+                        block_size=16, chunk=40, start_pos=(32,), chunk_lens=(40,), max_blocks_per_seq=6, seed=43)
+    log(f"[gpu] prefill with a bad block id, split={split}")
+    case = make_prefill_case(w)
+    bt = case.block_tables.copy()
+    bad = bt.copy()
+    bad[0, 1] = -1
+    dev = _to_dev(case)
+    dev["bt"].copy_(torch.from_numpy(bad))
+    out = _run(dev, w.scale, split)
+    got = as_f64(out)
+    kp, vp = oracle.kv_append_chunk(case.k_cache, case.v_cache, case.k_src, case.v_src, bt, case.start_pos,
+                                    case.chunk_lens, w.block_size)
+    remap = np.full_like(bt, -1)
+    remap[0, :4] = [bt[0, 0], bt[0, 2], bt[0, 3], bt[0, 4]]
+    atol, rtol = TOL["bf16"]
+    for i in range(40):
+        p = 32 + i
+        exp = oracle.paged_decode_attention(case.q[:, :, i, :], kp, vp, remap, np.array([p + 1 - 16], np.int32),
+                                            w.scale, w.block_size, "bf16")
+        assert_close(got[:, :, i], exp, atol, rtol, f"row {i} (position {p}) with a bad block id, split={split}")
