@@ -237,7 +237,7 @@ __device__ __forceinline__ void seq_partitions(const DecodeParams& prm, int b, i
 
 // Split items in the order that evens out the work per CU: full partitions first
 // (sequence-major, all the same size), then the partial last partitions by decreasing size (ties
-// by sequence; batches of more than 64 sequences keep sequence order). Workgroup k takes the item
+// by sequence). Workgroup k takes the item
 // whose rank is k with every second round of ncu consecutive ids reversed: with the whole grid
 // resident, ids k and k + ncu share a CU (the device deals workgroups to its CUs in turn), so a CU
 // that gets one of the larger partial items in one round gets one of the smaller ones in the
@@ -264,28 +264,63 @@ __device__ __forceinline__ void dense_item(const DecodeParams& prm, int k, int& 
   b = -1;
   p = 0;
   seg = 0;
-  if (!full && batch <= 64) {
-    // Rank of this lane's sequence among those with a partial partition, by decreasing size.
-    int nf = 0, np1 = 0;
-    if (lane < batch) seq_partitions<BS>(prm, lane, nf, np1);
-    const int L = lane < batch ? min(prm.context_lens[lane], prm.max_blocks_per_seq * BS) : 0;
-    const int nblk = L > 0 ? (L + BS - 1) / BS : 0;
-    const int key = np1 ? ((nblk - nf * prm.part_blocks) << 8) | (255 - lane) : -1;  // unique when >= 0
-    int rank = 0;
-    for (int jl = 0; jl < batch; ++jl) rank += __builtin_amdgcn_readlane(key, jl) > key ? 1 : 0;
-    const unsigned long long hit = __ballot(np1 && rank == k / segs);
-    if (hit) {
-      const int first = __builtin_ctzll(hit);
-      b = first;
-      p = __shfl(nf, first, 64);
-      seg = k % segs;
+  if (!full) {
+    // The sequence whose partial partition has rank r = k / segs by (size descending, index
+    // ascending). Partial sizes (in blocks, 0 for none) sit one per lane, 64 sequences per
+    // register; the size of rank r is found by binary search on counts taken with ballots, then
+    // the sequence among those of that size by index.
+    constexpr int kMaxChunks = kDenseMaxBatch / 64;
+    int psz[kMaxChunks], pnf[kMaxChunks];
+#pragma unroll
+    for (int ch = 0; ch < kMaxChunks; ++ch) {
+      psz[ch] = 0;
+      pnf[ch] = 0;
+      const int bb = 64 * ch + lane;
+      if (bb < batch) {
+        int nf = 0, np1 = 0;
+        seq_partitions<BS>(prm, bb, nf, np1);
+        const int L = min(prm.context_lens[bb], prm.max_blocks_per_seq * BS);
+        const int nblk = L > 0 ? (L + BS - 1) / BS : 0;
+        psz[ch] = np1 ? nblk - nf * prm.part_blocks : 0;
+        pnf[ch] = nf;
+      }
+    }
+    auto count_ge = [&](int sz) {  // partial partitions of at least sz blocks
+      int n = 0;
+#pragma unroll
+      for (int ch = 0; ch < kMaxChunks; ++ch) n += __builtin_popcountll(__ballot(psz[ch] >= sz));
+      return n;
+    };
+    const int r = k / segs;
+    if (r < count_ge(1)) {
+      int lo = 1, hi = prm.part_blocks - 1;  // the size of rank r lies in [lo, hi]
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (count_ge(mid) > r) lo = mid;
+        else hi = mid - 1;
+      }
+      int jth = r - count_ge(lo + 1);  // among the sequences of size lo, in index order
+#pragma unroll
+      for (int ch = 0; ch < kMaxChunks; ++ch) {
+        const unsigned long long m = __ballot(psz[ch] == lo);
+        const int cnt = __builtin_popcountll(m);
+        if (b < 0 && jth < cnt) {
+          const unsigned long long below = lane ? m & ((~0ull) >> (64 - lane)) : 0ull;
+          const unsigned long long hit = __ballot(((m >> lane) & 1ull) && __builtin_popcountll(below) == jth);
+          const int first = __builtin_ctzll(hit);
+          b = 64 * ch + first;
+          p = __shfl(pnf[ch], first, 64);
+          seg = k % segs;
+        }
+        jth -= cnt;
+      }
     }
   } else {
     int base = 0;
     for (int b0 = 0; b0 < batch && b < 0; b0 += 64) {
       int nf = 0, np1 = 0;
       if (b0 + lane < batch) seq_partitions<BS>(prm, b0 + lane, nf, np1);
-      const int own = (full ? nf : np1) * segs;
+      const int own = nf * segs;
       int incl = own;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -297,8 +332,8 @@ __device__ __forceinline__ void dense_item(const DecodeParams& prm, int k, int& 
         const int first = __builtin_ctzll(hit);
         const int r = k - base - __shfl(incl - own, first, 64);
         b = b0 + first;
-        p = full ? r / segs : __shfl(nf, first, 64);
-        seg = full ? r % segs : r;
+        p = r / segs;
+        seg = r % segs;
       } else {
         base += __shfl(incl, 63, 64);
       }
