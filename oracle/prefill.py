@@ -21,6 +21,16 @@ Readings where the pages are silent:
   and sees keys t in [0, p] (the bottom-right aligned mask of `flash_attention` with
   kv_len = start_pos[b] + chunk_lens[b]). With start_pos = 0 this is the pages' naive causal
   attention.
+
+Sinks and a sliding window (same diff, `flash_attention_sinks`: the prefill attention of the
+gpt-oss layers, always causal, one sink per query head folded into the softmax denominator,
+window_size 0 for full causal attention and > 0 for a sliding window), over the paged pool:
+
+* The window reads as in the decode with sinks: the query at position p keeps the last W
+  positions up to and including its own, t in [max(0, p + 1 - W), p]; W = 0 keeps [0, p].
+* The sink sigma_h of query head h is a logit in the units of the scaled scores and only enlarges
+  the denominator: out = sum_t e^(s_t - M) V_t / (e^(sigma_h - M) + sum_t e^(s_t - M)),
+  M = max(sigma_h, max_t s_t).
 """
 
 from __future__ import annotations
@@ -71,4 +81,52 @@ def paged_prefill_attention(q, k_cache, v_cache, block_tables, start_pos, chunk_
                 s = _scores(qv[b, h, i], K[g, :p + 1], scale)
                 w = np.exp(s - s.max())
                 out[b, h, i] = (w @ V[g, :p + 1]) / w.sum()
+    return out
+
+
+def window_first(p: int, window: int) -> int:
+    """First key position that the query at position p sees under a window of W (0: none)."""
+    return max(0, p + 1 - window) if window > 0 else 0
+
+
+def paged_prefill_attention_sinks(q, k_cache, v_cache, block_tables, start_pos, chunk_lens, scale, block_size,
+                                  dtype, sinks=None, window: int = 0):
+    """Chunked-prefill attention with per-head sinks and a sliding window, in fp64:
+    out[b, h, i] = sum_{t in [t0, p]} e^(s_t - M) V_t / (e^(sigma_h - M) + sum_{t in [t0, p]} e^(s_t - M))
+    with p = start_pos[b] + i, t0 = window_first(p, window), s_t = scale * q[b, h, i] . K_t and
+    M = max(sigma_h, max s_t); without sinks the sigma term is absent. Rows at or past
+    chunk_lens[b] are zero."""
+    qv = decode_values(q, dtype)
+    B, Hq, C, D = qv.shape
+    Hkv = k_cache.shape[1]
+    if Hq % Hkv != 0:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    if window < 0:
+        raise ValueError("window must be >= 0")
+    n_rep = Hq // Hkv
+    sig = None
+    if sinks is not None:
+        sig = decode_values(np.asarray(sinks), dtype)
+        if sig.shape != (Hq,):
+            raise ValueError("sinks must hold one value per query head")
+    out = np.zeros((B, Hq, C, D))
+    for b in range(B):
+        s0, n = int(start_pos[b]), int(chunk_lens[b])
+        if n <= 0:
+            continue
+        L = s0 + n
+        nblk = (L + block_size - 1) // block_size
+        ids = np.asarray(block_tables[b, :nblk], dtype=np.int64)
+        K = gather_kv(decode_values(k_cache[ids], dtype), np.arange(nblk), L, block_size)
+        V = gather_kv(decode_values(v_cache[ids], dtype), np.arange(nblk), L, block_size)
+        for h in range(Hq):
+            g = h // n_rep
+            for i in range(n):
+                p = s0 + i
+                t0 = window_first(p, window)
+                s = _scores(qv[b, h, i], K[g, t0:p + 1], scale)
+                M = s.max() if sig is None else max(s.max(), sig[h])
+                w = np.exp(s - M)
+                den = w.sum() + (0.0 if sig is None else np.exp(sig[h] - M))
+                out[b, h, i] = (w @ V[g, t0:p + 1]) / den
     return out
