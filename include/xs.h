@@ -364,6 +364,36 @@ int xs_paged_attn_prefill_split(const void* q, const void* k_cache, const void* 
                                 int dtype, void* stream);
 
 /*
+ * Chunked prefill attention with attention sinks and a sliding window, the prefill of the
+ * gpt-oss layers (xserv compare phase10...cf1e9e41, attention.rs, `flash_attention_sinks` and
+ * its FFI `launch_flash_attention_sinks_bf16`: always causal, one sink per query head folded
+ * into the softmax denominator, window_size 0 for full causal attention), over the paged pool
+ * as xs_paged_attn_prefill reads it.
+ *   sinks: NULL, or bf16 [num_q_heads] (device, read, 2-byte aligned): one logit sigma_h per
+ *          query head in the units of the scaled scores.
+ *   window_size: 0 keeps keys 0 .. p; W > 0 keeps keys max(0, p + 1 - W) .. p (the query's own
+ *          position and the W - 1 before it).
+ * Row i < chunk_lens[b] at position p = start_pos[b] + i, with t0 its first key, gets
+ *   out[b, h, i, :] = sum_{t0 <= t <= p} exp(s_t - M) V_t
+ *                     / (exp(sigma_h - M) + sum_{t0 <= t <= p} exp(s_t - M)),  M = max(sigma_h, max s_t)
+ * (no sigma term when sinks is NULL); other rows, invalid sequences and bad block ids as in
+ * xs_paged_attn_prefill. partition_size 0 computes each row block's keys in one workgroup
+ * (part_o and part_ml are not used and may be NULL); partition_size > 0 is the split-K of
+ * xs_paged_attn_prefill_split with the same partials and conditions, where the pieces carry no
+ * sink and the merge adds it once (M = max(sigma_h, max_j m_j), the sink a term of weight
+ * 2^(sigma_h log2e - M) with no value row), starting at the piece of the row's first window key.
+ * Readings where the pages are silent (window bounds, sink units, paged layout) are those of
+ * xs_paged_attn_decode_sinks. XS_BF16 only; window_size < 0 is XS_EINVAL. With sinks NULL and
+ * window_size 0 the result is that of xs_paged_attn_prefill / _split.
+ */
+int xs_paged_attn_prefill_sinks(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, const int32_t* start_pos, const int32_t* chunk_lens,
+                                const void* sinks, int window_size, float scale, void* out, float* part_o,
+                                float* part_ml, int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                int chunk_size, int block_size, int max_blocks_per_seq, int num_blocks,
+                                int partition_size, int max_partitions, int dtype, void* stream);
+
+/*
  * Measurement aid, not part of the decode step: reads `bytes` (a multiple of 16) at `buf` with
  * 16-byte loads (nontemporal if `nontemporal` != 0), each workgroup taking whole 64 KiB chunks,
  * and writes at most one word to `sink` (device memory, 4 bytes). Timing it gives the read rate

@@ -17,7 +17,8 @@ Contents:
 * ``sinks_window``: the same decode with per-head attention sinks and a
   sliding window, unsplit and split (the sink joins once, in the merge).
 * ``prefill``: the chunked-prefill step over the pools: multi-token append from a start
-  position, then causal (bottom-right aligned) attention of the chunk's queries.
+  position, then causal (bottom-right aligned) attention of the chunk's queries, also with
+  per-head sinks and a sliding window.
 * ``swap``: KV block swap-out / swap-in between the pools and host swap space
   (bit copies of whole blocks, list-driven).
 * ``brute_force``: the definitions again, in Python ``decimal`` at
@@ -40,7 +41,7 @@ from .paged_attention import (  # noqa: F401
     split_paged_decode_attention,
     naive_causal_attention,
 )
-from .prefill import kv_append_chunk, paged_prefill_attention  # noqa: F401
+from .prefill import kv_append_chunk, paged_prefill_attention, paged_prefill_attention_sinks  # noqa: F401
 from .sinks_window import (  # noqa: F401
     window_start,
     paged_decode_attention_sinks,

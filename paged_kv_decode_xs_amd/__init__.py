@@ -22,6 +22,7 @@ from ._binding import (  # noqa: F401
     xs_paged_attn_decode_balanced,
     xs_paged_attn_decode_sinks,
     xs_paged_attn_prefill,
+    xs_paged_attn_prefill_sinks,
     xs_paged_attn_prefill_split,
     xs_paged_attn_reduce,
     xs_paged_attn_reduce_sinks,

@@ -72,6 +72,8 @@ SIGNATURES = {
     "xs_paged_attn_prefill": [_vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp],
     "xs_paged_attn_prefill_split": [_vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
                                     _i, _i, _i, _vp],
+    "xs_paged_attn_prefill_sinks": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _f, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                                    _i, _i, _i, _i, _i, _vp],
     "xs_last_error": [],
     "xs_version": [],
 }
@@ -439,6 +441,49 @@ def xs_paged_attn_prefill_split(q: torch.Tensor, k_cache: torch.Tensor, v_cache:
     _check("xs_paged_attn_prefill_split", load_library().xs_paged_attn_prefill_split(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(start_pos), _ptr(chunk_lens), float(scale),
         _ptr(out), _ptr(part_o), _ptr(part_ml), B, Hq, Hkv, D, C, BS, MBPS, NB, int(partition_size), NP,
+        _dtype_code(q), _stream_handle(stream)))
+    return out
+
+
+def xs_paged_attn_prefill_sinks(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                block_tables: torch.Tensor, start_pos: torch.Tensor, chunk_lens: torch.Tensor,
+                                scale: float, sinks: Optional[torch.Tensor] = None, window_size: int = 0,
+                                partition_size: int = 0, out: Optional[torch.Tensor] = None,
+                                part_o: Optional[torch.Tensor] = None, part_ml: Optional[torch.Tensor] = None,
+                                stream=None) -> torch.Tensor:
+    """Chunked-prefill attention with per-head sinks (bf16 [Hq] or None) and a sliding window
+    (0: none); partition_size 0 runs unsplit, > 0 split-K with partials as in
+    xs_paged_attn_prefill_split (allocated here when not given)."""
+    _dev(q, k_cache, v_cache, block_tables, start_pos, chunk_lens, sinks, out, part_o, part_ml)
+    B, Hq, C, D = q.shape
+    NB, Hkv, BS, D2 = k_cache.shape
+    _need(D2 == D and v_cache.shape == k_cache.shape, "pool shapes do not match q")
+    _need(q.dtype == k_cache.dtype == v_cache.dtype, "q and the pools must have the same dtype")
+    _chunk_checks(B, block_tables, start_pos, chunk_lens)
+    if sinks is not None:
+        _need(sinks.shape == (Hq,) and sinks.dtype == torch.bfloat16 and sinks.is_contiguous(),
+              "sinks must be contiguous bfloat16 [num_q_heads]")
+    MBPS = block_tables.shape[1]
+    P = int(partition_size)
+    _need(P >= 0, "partition_size must be >= 0")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    NP = 0
+    if P > 0:
+        NP = num_partitions(MBPS * BS, P)
+        if part_o is None:
+            part_o = torch.empty((B, Hq, C, NP, D), dtype=torch.float32, device=q.device)
+        if part_ml is None:
+            part_ml = torch.empty((B, Hq, C, NP, 2), dtype=torch.float32, device=q.device)
+        _dev(part_o, part_ml)
+        _need(part_o.dtype == torch.float32 and part_ml.dtype == torch.float32 and part_o.is_contiguous()
+              and part_ml.is_contiguous(), "partials must be contiguous fp32")
+        NP = part_o.shape[3] if part_o.dim() == 5 else NP
+        _need(part_o.shape == (B, Hq, C, NP, D) and part_ml.shape == (B, Hq, C, NP, 2), "partial shapes do not match")
+    _check("xs_paged_attn_prefill_sinks", load_library().xs_paged_attn_prefill_sinks(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(start_pos), _ptr(chunk_lens), _ptr(sinks),
+        int(window_size), float(scale), _ptr(out), _ptr(part_o), _ptr(part_ml), B, Hq, Hkv, D, C, BS, MBPS, NB, P, NP,
         _dtype_code(q), _stream_handle(stream)))
     return out
 

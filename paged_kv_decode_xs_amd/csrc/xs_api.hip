@@ -520,7 +520,8 @@ static int prefill_common(const char* who, const void* q, const void* k_cache, c
                           const int32_t* block_tables, const int32_t* start_pos, const int32_t* chunk_lens,
                           float scale, void* out, float* part_o, float* part_ml, int batch, int num_q_heads,
                           int num_kv_heads, int head_dim, int chunk_size, int block_size, int max_blocks_per_seq,
-                          int num_blocks, int partition_size, int max_partitions, int dtype, void* stream) {
+                          int num_blocks, int partition_size, int max_partitions, int dtype, void* stream,
+                          const void* sinks = nullptr, int window = 0) {
   int st = check_pool_args(who, batch, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, dtype);
   if (st != XS_OK) return st;
   if (dtype != XS_BF16) return fail(XS_EUNSUPPORTED, "%s: only XS_BF16 is implemented", who);
@@ -530,6 +531,7 @@ static int prefill_common(const char* who, const void* q, const void* k_cache, c
                 num_kv_heads);
   if (chunk_size < 0) return fail(XS_EINVAL, "%s: chunk_size = %d < 0", who, chunk_size);
   if (!isfinite(scale)) return fail(XS_EINVAL, "%s: scale is not finite", who);
+  if (window < 0) return fail(XS_EINVAL, "%s: window_size = %d < 0", who, window);
   const int group = num_q_heads / num_kv_heads;
   if ((long long)chunk_size * group > 0x7fffffffLL - 64)
     return fail(XS_EINVAL, "%s: chunk_size * (num_q_heads / num_kv_heads) too large", who);
@@ -555,6 +557,7 @@ static int prefill_common(const char* who, const void* q, const void* k_cache, c
   if (split && (!part_o || !part_ml)) return fail(XS_EINVAL, "%s: part_o and part_ml are required", who);
   if (split && (!aligned16(part_o) || reinterpret_cast<uintptr_t>(part_ml) % 8 != 0))
     return fail(XS_EINVAL, "%s: part_o must be 16-byte and part_ml 8-byte aligned", who);
+  if (sinks && (reinterpret_cast<uintptr_t>(sinks) & 1u)) return fail(XS_EINVAL, "%s: sinks must be 2-byte aligned", who);
   xs::PrefillArgs a;
   a.q = q;
   a.k_cache = k_cache;
@@ -578,6 +581,8 @@ static int prefill_common(const char* who, const void* q, const void* k_cache, c
     a.partition_size = partition_size;
     a.max_partitions = max_partitions;
   }
+  a.sinks = sinks;
+  a.window = window;
   (void)hipGetLastError();
   return launch_status(who, xs::launch_paged_prefill(a, static_cast<hipStream_t>(stream)));
 }
@@ -603,4 +608,17 @@ XS_API int xs_paged_attn_prefill_split(const void* q, const void* k_cache, const
   return prefill_common(who, q, k_cache, v_cache, block_tables, start_pos, chunk_lens, scale, out, part_o, part_ml,
                         batch, num_q_heads, num_kv_heads, head_dim, chunk_size, block_size, max_blocks_per_seq,
                         num_blocks, partition_size, max_partitions, dtype, stream);
+}
+
+XS_API int xs_paged_attn_prefill_sinks(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, const int32_t* start_pos,
+                                       const int32_t* chunk_lens, const void* sinks, int window_size, float scale,
+                                       void* out, float* part_o, float* part_ml, int batch, int num_q_heads,
+                                       int num_kv_heads, int head_dim, int chunk_size, int block_size,
+                                       int max_blocks_per_seq, int num_blocks, int partition_size,
+                                       int max_partitions, int dtype, void* stream) {
+  return prefill_common("xs_paged_attn_prefill_sinks", q, k_cache, v_cache, block_tables, start_pos, chunk_lens,
+                        scale, out, part_o, part_ml, batch, num_q_heads, num_kv_heads, head_dim, chunk_size,
+                        block_size, max_blocks_per_seq, num_blocks, partition_size, max_partitions, dtype, stream,
+                        sinks, window_size);
 }

@@ -131,6 +131,9 @@ struct PrefillArgs {
   float* part_ml = nullptr;  // [B, Hq, C, max_partitions, 2]
   int partition_size = 0;    // keys per piece, a multiple of 64
   int max_partitions = 0;
+  // Sinks and a sliding window (bf16 [Hq] sink logits or null; window 0 = none).
+  const void* sinks = nullptr;
+  int window = 0;
 };
 // Row blocks per (sequence, kv head) of the prefill attention: chunk * group rows, 256 per block.
 int prefill_row_blocks(int chunk, int group);

@@ -28,6 +28,13 @@
 // block; a row block with several pieces leaves each row's normalised output over the piece and
 // its (max, sum) in the caller's partials, and the merge kernel combines them per row with the
 // log-sum-exp identity (the same as the decode's partition merge).
+// SW instances add the sinks and sliding window of the gpt-oss prefill (same diff,
+// `flash_attention_sinks`: one sink logit per query head that only enlarges the softmax
+// denominator; window_size W > 0 keeps the last W positions up to the query's own). A row at
+// position p sees keys max(0, p + 1 - W) .. p: the workgroup starts at the tile of its first
+// row's window, each wavefront skips the tiles before its own rows' windows, and the window's
+// lower edge joins the causal mask. The sink enters in the epilogue of an unsplit row, and in
+// the merge of a split one (pieces carry none).
 #include <math.h>
 
 #include "xs_internal.h"
@@ -83,6 +90,8 @@ struct PrefillParams {
   uint4* out;
   float* part_o;    // split only: [B, Hq, C, NP, D] f32, each row's output over one piece of keys
   float2* part_ml;  // split only: [B, Hq, C, NP] (m, l) of those pieces (m in scaled log2 units)
+  const uint16_t* sinks;  // SW only: [Hq] bf16 sink logits, or null
+  int window;             // SW only: W > 0 keeps positions p + 1 - W .. p; 0 keeps 0 .. p
   float scale_log2e;
   int batch, num_q_heads, num_kv_heads, group, chunk, row_blocks, bs_log2, max_blocks_per_seq, num_blocks;
   int part_tiles;      // key tiles per piece (0: each workgroup takes its whole key range)
@@ -138,7 +147,7 @@ __device__ __forceinline__ short4_lds_t lds_read_tr16(lds_byte* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_lds_t*)p);
 }
 
-template <int D>
+template <int D, bool SW>
 __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParams prm) {
   using LD = PrefillLds<D>;
   constexpr int ND = LD::ND;
@@ -200,8 +209,16 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
   const int PT = prm.part_tiles;
   const int npieces = PT > 0 ? (ntiles + PT - 1) / PT : 1;
   if (piece > 0 && piece >= npieces) return;
-  const int t_lo = PT > 0 ? piece * PT : 0;
-  const int t_hi = PT > 0 ? min(t_lo + PT, ntiles) : ntiles;
+  // Sliding window: the first tile that the workgroup's first row, and this wavefront's first
+  // row, see.
+  const int W = SW ? prm.window : 0;
+  const int tile_first = W > 0 ? max(0, s0 + rho0_wg / G + 1 - W) / kTileTokens : 0;
+  const int wave_first = W > 0 ? max(0, s0 + i_lo_wave + 1 - W) / kTileTokens : 0;
+  // Pieces wholly before the window leave at once (the merge starts each row at the piece of its
+  // window's first key, never earlier than this); piece 0 still writes its rows.
+  if (SW && piece > 0 && (piece + 1) * PT <= tile_first) return;
+  const int t_lo = SW ? max(PT > 0 ? piece * PT : 0, tile_first) : PT > 0 ? piece * PT : 0;
+  const int t_hi = PT > 0 ? min(piece * PT + PT, ntiles) : ntiles;
 
   float16_t acc[MD];
 #pragma unroll
@@ -306,7 +323,11 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
       // positions (vbits) up to the row's own position, none for rows outside the chunk. Tiles
       // that every row of the wavefront sees whole skip the masking.
       const int lim = pos_c - it * kTileTokens + 1;  // tokens 0 .. lim-1 are causal for this row
-      const uint64_t causal = lim >= 64 ? ~0ull : lim <= 0 ? 0ull : (1ull << lim) - 1ull;
+      uint64_t causal = lim >= 64 ? ~0ull : lim <= 0 ? 0ull : (1ull << lim) - 1ull;
+      if (W > 0) {
+        const int lo = lim - W;  // tokens before lo are outside this row's window
+        causal &= lo <= 0 ? ~0ull : lo >= 64 ? 0ull : ~((1ull << lo) - 1ull);
+      }
       const uint64_t allowed = row_valid ? vbits & causal : 0ull;
       float sc[32];
       if (__all(allowed == ~0ull)) {
@@ -389,7 +410,7 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
     auto step = [&](int it, TileRegs& nxt, TileRegs& fut, int& ids_now, int& ids_next) {
       ids_next = tile_ids(it + 3);
       load_tile(it + 2, ids_now, fut);
-      if (it < wave_tiles) compute(it, vbits);
+      if (it < wave_tiles && (!SW || it >= wave_first)) compute(it, vbits);
       store_tile((it + 1) & 1, nxt);
       __syncthreads();
       vbits = nxt.vbits;
@@ -415,7 +436,12 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
   const float2 lp = with_other_half(l_part);
   const float l_tot = lp.x + lp.y;
   if (!row_exists) return;
-  const float inv = row_valid && l_tot > 0.f ? 1.f / l_tot : 0.f;
+  // The sink of an unsplit row: e^(sigma - m) more in the denominator (in log2 units; a row with
+  // no keys keeps its zeros).
+  float den = l_tot;
+  if (SW && prm.sinks && npieces <= 1 && m_run != -INFINITY)
+    den += fast_exp2(bf16lo_to_f32(prm.sinks[h_c]) * kLog2e - m_run);
+  const float inv = row_valid && den > 0.f ? 1.f / den : 0.f;
   // acc[md][r] is O[row n][32md + 8(r/4) + 4hl + r%4]: four runs of 4 values per d block.
   if (npieces > 1 && row_valid) {
     // A piece of a split row block: this row's output over the piece's keys, and its (m, l)
@@ -449,9 +475,10 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
 // kernel): 32 lanes per row, four consecutive d each. Row (b, h, i) combines the pieces that hold
 // keys it sees (pieces 0 .. pos / (64 PT)): M = max_j m_j, w_j = l_j 2^(m_j - M),
 // out = sum_j w_j o_j / sum_j w_j, taken four pieces at a time (their loads in flight together)
-// with a running maximum.
+// with a running maximum. SW: the pieces start at the one holding the row's first window key,
+// and the sink enters as one more term of weight 2^(sigma - M) with no value row.
 constexpr int kMergeThreads = 256;
-template <int D>
+template <int D, bool SW>
 __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillParams prm) {
   constexpr int LPR = D / 4;                  // lanes per row
   constexpr int RPB = kMergeThreads / LPR;  // rows per workgroup
@@ -475,8 +502,16 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillPar
   const int nrow = (s0 + i) / (kTileTokens * PT) + 1;  // pieces holding keys 0 .. s0 + i
   const size_t prow0 = (size_t)row * prm.max_partitions;
   float M = -INFINITY, wsum = 0.f;
+  int jfirst = 0;
+  if (SW) {
+    if (prm.window > 0) jfirst = max(0, s0 + i + 1 - prm.window) / (kTileTokens * PT);
+    if (prm.sinks) {
+      M = bf16lo_to_f32(prm.sinks[h]) * kLog2e;  // the sink's term, 2^(sigma - M) = 1
+      wsum = 1.f;
+    }
+  }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j0 = 0; j0 < nrow; j0 += 4) {
+  for (int j0 = jfirst; j0 < nrow; j0 += 4) {
     float2 ml[4];
     float4 o[4];
 #pragma unroll
@@ -507,16 +542,16 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillPar
       make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
 }
 
-template <int D>
+template <int D, bool SW>
 hipError_t launch_prefill_d(const PrefillParams& p, hipStream_t stream) {
   const long long pieces = p.part_tiles > 0 ? p.max_partitions : 1;
   const long long grid = (long long)p.batch * p.num_kv_heads * p.row_blocks * pieces;
-  hipLaunchKernelGGL(paged_prefill_kernel<D>, dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, p);
+  hipLaunchKernelGGL((paged_prefill_kernel<D, SW>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, p);
   if (p.part_tiles > 0) {
     const long long rows = (long long)p.batch * p.num_q_heads * p.chunk;
     constexpr int rpb = kMergeThreads / (D / 4);
-    hipLaunchKernelGGL(prefill_merge_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(kMergeThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL((prefill_merge_kernel<D, SW>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(kMergeThreads),
+                       0, stream, p);
   }
   return hipGetLastError();
 }
@@ -563,7 +598,11 @@ hipError_t launch_paged_prefill(const PrefillArgs& a, hipStream_t stream) {
   p.bs_log2 = a.block_size == 8 ? 3 : a.block_size == 16 ? 4 : 5;
   p.max_blocks_per_seq = a.max_blocks_per_seq;
   p.num_blocks = a.num_blocks;
-  return a.head_dim == 64 ? launch_prefill_d<64>(p, stream) : launch_prefill_d<128>(p, stream);
+  p.sinks = static_cast<const uint16_t*>(a.sinks);
+  p.window = a.window;
+  if (a.sinks || a.window > 0)
+    return a.head_dim == 64 ? launch_prefill_d<64, true>(p, stream) : launch_prefill_d<128, true>(p, stream);
+  return a.head_dim == 64 ? launch_prefill_d<64, false>(p, stream) : launch_prefill_d<128, false>(p, stream);
 }
 
 }  // namespace xs

@@ -374,3 +374,35 @@ def test_prefill_split_empty_is_a_noop():
 def test_prefill_empty_is_a_noop():
     assert _prefill(batch=0, q=None, out=None) == 0
     assert _prefill(c=0, q=None, out=None) == 0
+
+
+def _prefill_sinks(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sp=FAKE, cl=FAKE, sinks=FAKE, w=128, scale=0.125, out=FAKE, po=None,
+             pml=None, batch=2, hq=8, hkv=2, d=64, c=16, bs=16, mbps=4, nb=16, p=0, np_=0, dt=B)
+    a.update(kw)
+    return xb.load_library().xs_paged_attn_prefill_sinks(
+        a["q"], a["kc"], a["vc"], a["bt"], a["sp"], a["cl"], a["sinks"], a["w"], a["scale"], a["out"], a["po"],
+        a["pml"], a["batch"], a["hq"], a["hkv"], a["d"], a["c"], a["bs"], a["mbps"], a["nb"], a["p"], a["np_"],
+        a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(w=-1), 1, "window_size = -1"),
+    (dict(sinks=FAKE + 1), 1, "sinks must be 2-byte aligned"),
+    (dict(dt=F), 2, "XS_BF16"),
+    (dict(d=96), 2, "head_dim"),
+    (dict(hq=6, hkv=4), 1, "multiple"),
+    (dict(p=96, np_=1), 1, "multiple of 64"),
+    (dict(p=64, np_=1), 1, "part_o and part_ml"),
+    (dict(p=64, np_=0, po=FAKE, pml=FAKE), 1, "max_partitions = 0 < 1"),
+    (dict(out=None), 1, "NULL"),
+    (dict(scale=float("inf")), 1, "scale"),
+])
+def test_prefill_sinks_rejects(kw, status, needle):
+    assert _prefill_sinks(**kw) == status
+    assert needle in xb.xs_last_error()
+
+
+def test_prefill_sinks_empty_is_a_noop():
+    assert _prefill_sinks(batch=0, q=None, out=None) == 0
+    assert _prefill_sinks(c=0, q=None, out=None, p=64, np_=1) == 0

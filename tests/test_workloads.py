@@ -110,6 +110,17 @@ def test_prefill_key_visits_and_flops():
     assert w.append_bytes() == 2 * 2 * 27 * 2 * 64 * 2
 
 
+def test_prefill_key_visits_with_a_window_and_sinks_drawn_last():
+    w = _tiny_prefill(window=9)
+    brute = sum(len(range(max(0, s0 + i + 1 - 9), s0 + i + 1)) for s0, n in zip(w.start_pos, w.chunk_lens)
+                for i in range(n))
+    assert w.key_visits() == brute
+    a, b = make_prefill_case(_tiny_prefill()), make_prefill_case(_tiny_prefill(sinks=True))
+    assert a.sinks is None and b.sinks.shape == (4,) and b.sinks.dtype == np.uint16
+    for f in ("q", "k_src", "v_src", "k_cache", "v_cache", "block_tables"):
+        assert np.array_equal(getattr(a, f), getattr(b, f))  # the sinks do not move the other draws
+
+
 def test_prefill_workloads_are_valid():
     for w in PREFILL_WORKLOADS.values():
         assert w.batch == len(w.chunk_lens)

@@ -16,6 +16,8 @@ Recipe:
    batch order. Rows past chunk_lens[b] are drawn too (and must be ignored).
 4. Poison: every pool slot at a position >= start_pos[b] (the chunk's own slots, which the
    append must fill, and the tail) and every unused block is NaN.
+5. Workloads with sinks (the gpt-oss layers): last, one sink logit per query head, float32
+   N(0, 1) rounded to bf16. The window is a fixed size of the workload.
 """
 
 from __future__ import annotations
@@ -44,6 +46,8 @@ class PrefillWorkload:
     max_blocks_per_seq: int
     seed: int
     num_blocks: Optional[int] = None
+    window: int = 0  # sliding window W (0: full causal attention)
+    sinks: bool = False  # one sink logit per query head
 
     @property
     def batch(self) -> int:
@@ -65,11 +69,15 @@ class PrefillWorkload:
         return dataclasses.replace(self, **kw)
 
     def key_visits(self) -> int:
-        """sum over chunk rows (b, i < n_b) of the keys the row sees, start_pos[b] + i + 1 (one head)."""
+        """sum over chunk rows (b, i < n_b) of the keys the row sees (one head): start_pos[b] + i + 1,
+        at most W with a sliding window."""
         tot = 0
         for s0, n in zip(self.start_pos, self.chunk_lens):
             n = max(int(n), 0)
-            tot += n * (int(s0) + 1) + n * (n - 1) // 2
+            if self.window > 0:
+                tot += sum(min(int(s0) + i + 1, self.window) for i in range(n))
+            else:
+                tot += n * (int(s0) + 1) + n * (n - 1) // 2
         return tot
 
     def attention_flops(self) -> int:
@@ -93,6 +101,7 @@ class PrefillCase:
     block_tables: np.ndarray  # int32 [B, MBPS]
     start_pos: np.ndarray  # int32 [B]
     chunk_lens: np.ndarray  # int32 [B]
+    sinks: Optional[np.ndarray] = None  # bf16 bits [Hq] when the workload has sinks
 
 
 PREFILL_WORKLOADS: Dict[str, PrefillWorkload] = {
@@ -112,6 +121,23 @@ PREFILL_WORKLOADS: Dict[str, PrefillWorkload] = {
             "128, block_size 16 (64 row blocks: the split-K case)",
             dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, chunk=512,
             start_pos=(15872,), chunk_lens=(512,), max_blocks_per_seq=1024, seed=7,
+        ),
+        PrefillWorkload(
+            name="gptoss_20b_prefill_window128_c512",
+            description="gpt-oss-20b sliding-window layer shape, bf16 chunked prefill: 4 sequences, 512-token "
+            "chunks starting at 0, 1024, 2048 and 3584 cached tokens, 64 q / 8 KV heads, head_dim 64, "
+            "block_size 16, a 128-token window and one sink per query head",
+            dtype="bf16", num_q_heads=64, num_kv_heads=8, head_dim=64, block_size=16, chunk=512,
+            start_pos=(0, 1024, 2048, 3584), chunk_lens=(512, 512, 512, 512), max_blocks_per_seq=256, seed=8,
+            window=128, sinks=True,
+        ),
+        PrefillWorkload(
+            name="gptoss_20b_prefill_full_c512",
+            description="gpt-oss-20b full-attention layer shape, bf16 chunked prefill: the same 4 sequences and "
+            "chunks, 64 q / 8 KV heads, head_dim 64, block_size 16, no window, one sink per query head",
+            dtype="bf16", num_q_heads=64, num_kv_heads=8, head_dim=64, block_size=16, chunk=512,
+            start_pos=(0, 1024, 2048, 3584), chunk_lens=(512, 512, 512, 512), max_blocks_per_seq=256, seed=9,
+            sinks=True,
         ),
     ]
 }
@@ -157,8 +183,9 @@ def make_prefill_case(w: PrefillWorkload, seed: Optional[int] = None) -> Prefill
         flat_v[int(s0[b]):] = _nan_fill((), w.dtype)
         k_cache[ids] = flat_k.reshape(nb, BS, Hkv, D).transpose(0, 2, 1, 3)
         v_cache[ids] = flat_v.reshape(nb, BS, Hkv, D).transpose(0, 2, 1, 3)
+    sinks = _encode(_normal(rng, (Hq,)), w.dtype) if w.sinks else None
     return PrefillCase(workload=w, q=q, k_src=k_src, v_src=v_src, k_cache=k_cache, v_cache=v_cache,
-                       block_tables=bt, start_pos=s0.astype(np.int32), chunk_lens=n.astype(np.int32))
+                       block_tables=bt, start_pos=s0.astype(np.int32), chunk_lens=n.astype(np.int32), sinks=sinks)
 
 
 PREFILL_ORDER: List[str] = list(PREFILL_WORKLOADS)
