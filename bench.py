@@ -428,7 +428,12 @@ def swap_row(reps: int = 10) -> dict:
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-PREFILL_SPLITS = {"qwen3_8b_prefill_c512": (1024, 2048), "qwen3_8b_prefill_long16k": (1024, 2048, 4096)}
+PREFILL_SPLITS = {"qwen3_8b_prefill_c512": (1024, 2048), "qwen3_8b_prefill_long16k": (1024, 2048, 4096),
+                  "gptoss_20b_prefill_full_c512": (1024, 2048)}
+# Prefill rows of the result line: key -> workload.
+PREFILL_ROWS = {"chunked_prefill": "qwen3_8b_prefill_c512", "chunked_prefill_long": "qwen3_8b_prefill_long16k",
+                "chunked_prefill_gptoss_window": "gptoss_20b_prefill_window128_c512",
+                "chunked_prefill_gptoss_full": "gptoss_20b_prefill_full_c512"}
 
 
 def prefill_row(name: str = "qwen3_8b_prefill_c512", reps: int = 20, partitions=None) -> dict:
@@ -440,6 +445,9 @@ def prefill_row(name: str = "qwen3_8b_prefill_c512", reps: int = 20, partitions=
     object is the fastest of them. It is a dense contraction on the matrix cores: algorithmic flops
     (4 * head_dim per (query head, chunk row, visible key)) over its time, against the bf16 dense
     MFMA peak. The append moves bytes: read + write of every chunk row, against HBM peak.
+    Workloads with sinks or a sliding window (the gpt-oss layers) go through
+    xs_paged_attn_prefill_sinks, whole and split alike; their flops count only the keys inside
+    each row's window.
     `partitions` (a list, 0 = the whole call) restricts the timed paths, for profiling one."""
     import torch
 
@@ -458,6 +466,17 @@ def prefill_row(name: str = "qwen3_8b_prefill_c512", reps: int = 20, partitions=
     cl = torch.from_numpy(case.chunk_lens).cuda()
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
+    sw = w.window > 0 or w.sinks
+    sinks = None if case.sinks is None else to_torch(case.sinks, dt).cuda()
+
+    def attend(P, out_, po=None, pml=None):
+        if sw:
+            return xs.xs_paged_attn_prefill_sinks(q, kc, vc, bt, sp, cl, w.scale, sinks=sinks, window_size=w.window,
+                                                  partition_size=P, out=out_, part_o=po, part_ml=pml, stream=stream)
+        if P == 0:
+            return xs.xs_paged_attn_prefill(q, kc, vc, bt, sp, cl, w.scale, out=out_, stream=stream)
+        return xs.xs_paged_attn_prefill_split(q, kc, vc, bt, sp, cl, w.scale, P, out=out_, part_o=po, part_ml=pml,
+                                              stream=stream)
 
     def med(fn):
         for _ in range(3):
@@ -483,15 +502,14 @@ def prefill_row(name: str = "qwen3_8b_prefill_c512", reps: int = 20, partitions=
     by_p = {}
     finite = True
     if 0 in paths:
-        by_p[0] = med(lambda: xs.xs_paged_attn_prefill(q, kc, vc, bt, sp, cl, w.scale, out=out, stream=stream))
+        by_p[0] = med(lambda: attend(0, out))
         finite = bool(torch.isfinite(out.float()).all().item())
     for P in (p for p in paths if p):
         NP = xs.num_partitions(bt.shape[1] * kc.shape[2], P)
         po = torch.empty((*q.shape[:3], NP, q.shape[3]), dtype=torch.float32, device="cuda")
         pml = torch.empty((*q.shape[:3], NP, 2), dtype=torch.float32, device="cuda")
         out_s = torch.empty_like(q)
-        by_p[P] = med(lambda: xs.xs_paged_attn_prefill_split(q, kc, vc, bt, sp, cl, w.scale, P, out=out_s, part_o=po,
-                                                             part_ml=pml, stream=stream))
+        by_p[P] = med(lambda: attend(P, out_s, po, pml))
         finite = finite and bool(torch.isfinite(out_s.float()).all().item())
         del po, pml, out_s
     best_p = min(by_p, key=by_p.get)
@@ -504,6 +522,8 @@ def prefill_row(name: str = "qwen3_8b_prefill_c512", reps: int = 20, partitions=
         "workload": w.name,
         "description": w.description,
         "chunk_rows": int(case.chunk_lens.sum()),
+        "window": w.window,
+        "sinks": bool(w.sinks),
         "roofline": {
             "bound": "mfma",
             "achieved": round(tflops, 2),
@@ -511,8 +531,9 @@ def prefill_row(name: str = "qwen3_8b_prefill_c512", reps: int = 20, partitions=
             "unit": "TFLOP/s",
             "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": None,
-            "kernel": "paged_prefill_kernel" if best_p == 0 else
-                      f"paged_prefill_kernel + prefill_merge_kernel (split-K, partition_size {best_p})",
+            "kernel": ("paged_prefill_kernel" if best_p == 0 else
+                       f"paged_prefill_kernel + prefill_merge_kernel (split-K, partition_size {best_p})")
+                      + (" (sinks/window instance)" if sw else ""),
             "algorithmic_flops_per_launch": flops,
             "median_launch_us": round(attn_ms * 1e3, 2),
         },
@@ -596,8 +617,7 @@ def main() -> int:
     if args.prefill_only:
         reps = max(args.steps, 5)
         parts = None if args.prefill_partition is None else [args.prefill_partition]
-        rows = {"chunked_prefill": "qwen3_8b_prefill_c512", "chunked_prefill_long": "qwen3_8b_prefill_long16k"}
-        print(json.dumps({k: prefill_row(n, reps=reps, partitions=parts) for k, n in rows.items()
+        print(json.dumps({k: prefill_row(n, reps=reps, partitions=parts) for k, n in PREFILL_ROWS.items()
                           if args.prefill_workload in (None, n)}), flush=True)
         return 0
 
@@ -705,9 +725,9 @@ def main() -> int:
                                   run_workload(we, we.partition_size, fused, min(K, 100), args.warmup)))
         result["extra_workloads"] = rows
         result["kv_swap"] = swap_row()
-        result["chunked_prefill"] = prefill_row()
-        torch.cuda.empty_cache()
-        result["chunked_prefill_long"] = prefill_row("qwen3_8b_prefill_long16k")
+        for key, name in PREFILL_ROWS.items():
+            result[key] = prefill_row(name)
+            torch.cuda.empty_cache()
         result["graph_replay"] = [graph_row(wl.WORKLOADS[name], layers, min(K, 50), min(args.warmup, 5))
                                   for name, layers in GRAPH_WORKLOADS]
     print(json.dumps(result), flush=True)
