@@ -147,6 +147,110 @@ __device__ __forceinline__ short4_lds_t lds_read_tr16(lds_byte* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_lds_t*)p);
 }
 
+// Key tiles of row block rb (256 rows) of sequence b: up to its last valid row's position (0 when
+// the row block holds no valid row or the sequence's range is invalid).
+__device__ __forceinline__ int row_block_tiles(const PrefillParams& prm, int b, int rb) {
+  const int BS = 1 << prm.bs_log2;
+  int s0 = prm.start_pos[b], nlen = prm.chunk_lens[b];
+  if (s0 < 0 || nlen < 0 || nlen > prm.chunk || (long long)s0 + nlen > (long long)prm.max_blocks_per_seq * BS) return 0;
+  const int rows_total = prm.chunk * prm.group;
+  const int rho0 = rb * kRowsPerGroup;
+  const int i_hi = min((min(rho0 + kRowsPerGroup, rows_total) - 1) / prm.group, nlen - 1);
+  return i_hi >= rho0 / prm.group ? (s0 + i_hi) / kTileTokens + 1 : 0;
+}
+
+// Split-K item of rank k (per kv head), largest first: the full pieces (PT tiles) of every row
+// block, then each row block's last piece (fewer tiles, or none: a row block without keys still
+// has its piece 0, which writes its zero rows) by decreasing size, ties by row block. Row block
+// x = b * row_blocks + (row_blocks - 1 - rb). One wavefront holds the row blocks' sizes, 64 to a
+// register (up to kRankMax row blocks), and finds the size of rank k by a binary search on
+// ballot counts. Sets b = -1 past the last item.
+constexpr int kRankMax = 256;
+__device__ __forceinline__ void ranked_piece(const PrefillParams& prm, int k, int& b, int& rb, int& piece) {
+  const int lane = threadIdx.x & 63;
+  const int PT = prm.part_tiles, RBN = prm.row_blocks;
+  const int nx = prm.batch * RBN;
+  constexpr int kChunks = kRankMax / 64;
+  int nfull[kChunks], last[kChunks];  // full pieces; size of the last piece (-1: none)
+  int F = 0;
+#pragma unroll
+  for (int ch = 0; ch < kChunks; ++ch) {
+    nfull[ch] = 0;
+    last[ch] = -1;
+    const int x = 64 * ch + lane;
+    if (x < nx) {
+      const int nt = row_block_tiles(prm, x / RBN, RBN - 1 - x % RBN);
+      nfull[ch] = nt / PT;
+      last[ch] = nt % PT != 0 || nt == 0 ? nt % PT : -1;
+    }
+    int f = nfull[ch];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) f += __shfl_xor(f, off, 64);
+    F += f;
+  }
+  b = -1;
+  rb = 0;
+  piece = 0;
+  int x = -1;
+  if (k < F) {
+    // The k-th full piece, row block major.
+    int base = 0;
+#pragma unroll
+    for (int ch = 0; ch < kChunks; ++ch) {
+      int incl = nfull[ch];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      const unsigned long long hit = __ballot(base + incl > k);
+      if (x < 0 && hit) {
+        const int first = __builtin_ctzll(hit);
+        x = 64 * ch + first;
+        piece = k - base - __shfl(incl - nfull[ch], first, 64);
+      }
+      base += __shfl(incl, 63, 64);
+    }
+  } else {
+    const int r = k - F;
+    auto count_ge = [&](int sz) {
+      int cnt = 0;
+#pragma unroll
+      for (int ch = 0; ch < kChunks; ++ch) cnt += __builtin_popcountll(__ballot(last[ch] >= sz));
+      return cnt;
+    };
+    if (r < count_ge(0)) {
+      int lo = 0, hi = PT - 1;  // the size of rank r lies in [lo, hi]
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (count_ge(mid) > r) lo = mid;
+        else hi = mid - 1;
+      }
+      int jth = r - count_ge(lo + 1);
+#pragma unroll
+      for (int ch = 0; ch < kChunks; ++ch) {
+        const unsigned long long m = __ballot(last[ch] == lo);
+        const int cnt = __builtin_popcountll(m);
+        if (x < 0 && jth < cnt) {
+          const unsigned long long below = lane ? m & ((~0ull) >> (64 - lane)) : 0ull;
+          const unsigned long long hit = __ballot(((m >> lane) & 1ull) && __builtin_popcountll(below) == jth);
+          const int first = __builtin_ctzll(hit);
+          x = 64 * ch + first;
+          piece = __shfl(nfull[ch], first, 64);
+        }
+        jth -= cnt;
+      }
+    }
+  }
+  if (x >= 0) {
+    b = x / RBN;
+    rb = RBN - 1 - x % RBN;
+  }
+  b = __builtin_amdgcn_readfirstlane(b);
+  rb = __builtin_amdgcn_readfirstlane(rb);
+  piece = __builtin_amdgcn_readfirstlane(piece);
+}
+
 template <int D, bool SW>
 __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParams prm) {
   using LD = PrefillLds<D>;
@@ -167,13 +271,21 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
   // engines of an XCD take row blocks of every sequence and piece alike (similar work, no engine
   // holding up the queue), and the workgroups of one kv head share an XCD's L2 when the number of
   // kv heads is a multiple of 8.
+  // With split-K and at most kRankMax row blocks per kv head, the pieces go largest first
+  // (ranked_piece), kv head still fastest.
   const int Hkv_ = prm.num_kv_heads;
   const int g = (int)(blockIdx.x % (unsigned)Hkv_);
   const int r1 = (int)(blockIdx.x / (unsigned)Hkv_);
-  const int rb = prm.row_blocks - 1 - r1 % prm.row_blocks;
-  const int r2 = r1 / prm.row_blocks;
-  const int b = r2 % prm.batch;
-  const int piece = r2 / prm.batch;
+  int rb, b, piece;
+  if (prm.part_tiles > 0 && prm.batch * prm.row_blocks <= kRankMax) {
+    ranked_piece(prm, r1, b, rb, piece);
+    if (b < 0) return;
+  } else {
+    rb = prm.row_blocks - 1 - r1 % prm.row_blocks;
+    const int r2 = r1 / prm.row_blocks;
+    b = r2 % prm.batch;
+    piece = r2 / prm.batch;
+  }
   const int G = prm.group;
   const int C = prm.chunk;
   const int BS = 1 << prm.bs_log2;
