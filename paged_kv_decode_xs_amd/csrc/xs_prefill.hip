@@ -96,6 +96,7 @@ struct PrefillParams {
   int batch, num_q_heads, num_kv_heads, group, chunk, row_blocks, bs_log2, max_blocks_per_seq, num_blocks;
   int part_tiles;      // key tiles per piece (0: each workgroup takes its whole key range)
   int max_partitions;  // NP
+  int rank_items;      // 1: workgroups take row blocks / pieces largest first (ranked_piece)
 };
 
 typedef float __attribute__((ext_vector_type(16))) float16_t;
@@ -159,16 +160,17 @@ __device__ __forceinline__ int row_block_tiles(const PrefillParams& prm, int b, 
   return i_hi >= rho0 / prm.group ? (s0 + i_hi) / kTileTokens + 1 : 0;
 }
 
-// Split-K item of rank k (per kv head), largest first: the full pieces (PT tiles) of every row
-// block, then each row block's last piece (fewer tiles, or none: a row block without keys still
-// has its piece 0, which writes its zero rows) by decreasing size, ties by row block. Row block
+// Item of rank k (per kv head), largest first: with split-K the full pieces (PT tiles) of every
+// row block, then each row block's last piece (fewer tiles, or none: a row block without keys
+// still has its piece 0, which writes its zero rows) by decreasing size, ties by row block;
+// without split-K the row blocks themselves by decreasing size. Row block
 // x = b * row_blocks + (row_blocks - 1 - rb). One wavefront holds the row blocks' sizes, 64 to a
 // register (up to kRankMax row blocks), and finds the size of rank k by a binary search on
 // ballot counts. Sets b = -1 past the last item.
 constexpr int kRankMax = 256;
 __device__ __forceinline__ void ranked_piece(const PrefillParams& prm, int k, int& b, int& rb, int& piece) {
   const int lane = threadIdx.x & 63;
-  const int PT = prm.part_tiles, RBN = prm.row_blocks;
+  const int PT = prm.part_tiles > 0 ? prm.part_tiles : 1 << 24, RBN = prm.row_blocks;
   const int nx = prm.batch * RBN;
   constexpr int kChunks = kRankMax / 64;
   int nfull[kChunks], last[kChunks];  // full pieces; size of the last piece (-1: none)
@@ -219,8 +221,13 @@ __device__ __forceinline__ void ranked_piece(const PrefillParams& prm, int k, in
       for (int ch = 0; ch < kChunks; ++ch) cnt += __builtin_popcountll(__ballot(last[ch] >= sz));
       return cnt;
     };
+    int top = 0;  // largest last-piece size
+#pragma unroll
+    for (int ch = 0; ch < kChunks; ++ch) top = max(top, last[ch]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) top = max(top, __shfl_xor(top, off, 64));
     if (r < count_ge(0)) {
-      int lo = 0, hi = PT - 1;  // the size of rank r lies in [lo, hi]
+      int lo = 0, hi = top;  // the size of rank r lies in [lo, hi]
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (count_ge(mid) > r) lo = mid;
@@ -271,13 +278,13 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
   // engines of an XCD take row blocks of every sequence and piece alike (similar work, no engine
   // holding up the queue), and the workgroups of one kv head share an XCD's L2 when the number of
   // kv heads is a multiple of 8.
-  // With split-K and at most kRankMax row blocks per kv head, the pieces go largest first
+  // With rank_items (set by the launcher) the row blocks or split-K pieces go largest first
   // (ranked_piece), kv head still fastest.
   const int Hkv_ = prm.num_kv_heads;
   const int g = (int)(blockIdx.x % (unsigned)Hkv_);
   const int r1 = (int)(blockIdx.x / (unsigned)Hkv_);
   int rb, b, piece;
-  if (prm.part_tiles > 0 && prm.batch * prm.row_blocks <= kRankMax) {
+  if (prm.rank_items) {
     ranked_piece(prm, r1, b, rb, piece);
     if (b < 0) return;
   } else {
@@ -712,6 +719,13 @@ hipError_t launch_paged_prefill(const PrefillArgs& a, hipStream_t stream) {
   p.num_blocks = a.num_blocks;
   p.sinks = static_cast<const uint16_t*>(a.sinks);
   p.window = a.window;
+  // Largest first where the order matters and the sizes differ: split-K pieces (always more
+  // workgroups than CUs' worth of work at once), or unsplit row blocks when the grid exceeds
+  // one workgroup per CU (the resident limit at these register counts) and there is no window
+  // (windowed row blocks are all alike, and the ranking would only add latency). The ranking
+  // covers up to kRankMax row blocks per kv head.
+  const long long rbs = (long long)p.batch * p.row_blocks;
+  p.rank_items = rbs <= kRankMax && (p.part_tiles > 0 || (rbs * p.num_kv_heads > device_cu_count() && p.window == 0));
   if (a.sinks || a.window > 0)
     return a.head_dim == 64 ? launch_prefill_d<64, true>(p, stream) : launch_prefill_d<128, true>(p, stream);
   return a.head_dim == 64 ? launch_prefill_d<64, false>(p, stream) : launch_prefill_d<128, false>(p, stream);
