@@ -16,7 +16,9 @@ output for the same queries on the
 same pools (twice the bf16 bar: each is within it of the oracle). The split-K entry point
 (xs_paged_attn_prefill_split) is held to the same bar with partition
 sizes of 64 and 128 keys, so the small shapes already split into several pieces and rows see
-pieces with and without keys of their own.
+pieces with and without keys of their own. Two shapes cover the workgroup orders in full: 448
+workgroups of mixed sizes (taken largest first, unsplit and split, with an empty and an invalid
+sequence), and 264 row blocks per kv head (the fixed order).
 """
 
 import numpy as np
@@ -128,6 +130,45 @@ def test_prefill_matches_oracle(shape):
 def test_prefill_split_matches_oracle(shape, split):
     Hq, Hkv, D, BS, C = shape[:5]
     _full_check(_shape_workload(shape), f"Hq{Hq} Hkv{Hkv} D{D} BS{BS} C{C}", split)
+
+
+# Dispatch orders: many row blocks of mixed sizes in a grid larger than one workgroup per CU
+# (the unsplit row blocks and the split-K pieces are taken largest first, a sequence without rows
+# and an invalid one still get their zero rows), and more than 256 row blocks per kv head (the
+# fixed order).
+ORDER_SHAPES = {
+    "ranked": (64, 16, 64, 16, 200, (0, 300, 50, 700, 0, 10, -5), (200, 64, 0, 200, 33, 200, 10)),
+    "fixed": (8, 1, 128, 16, 2100, (0, 37, 900, 5), (2100, 1500, 2100, 7)),
+}
+
+
+@pytest.mark.parametrize("split", [None, 64, 256])
+@pytest.mark.parametrize("order", sorted(ORDER_SHAPES))
+def test_prefill_dispatch_orders(order, split):
+    Hq, Hkv, D, BS, C, sp, cl = ORDER_SHAPES[order]
+    mbps = -(-max(max(s, 0) + n for s, n in zip(sp, cl)) // BS) + 2
+    w = PrefillWorkload(name="t", description="", dtype="bf16", num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                        block_size=BS, chunk=C, start_pos=tuple(max(s, 0) for s in sp), chunk_lens=cl,
+                        max_blocks_per_seq=mbps, seed=31 if order == "ranked" else 32)
+    row_blocks = -(-C * (Hq // Hkv) // 256)
+    assert (len(sp) * row_blocks <= 256) == (order == "ranked")
+    log(f"[gpu] prefill dispatch order {order}: {len(sp)} seqs x {row_blocks} row blocks x {Hkv} kv heads, split={split}")
+    case = make_prefill_case(w)
+    kp, vp = oracle.kv_append_chunk(case.k_cache, case.v_cache, case.k_src, case.v_src, case.block_tables,
+                                    case.start_pos, case.chunk_lens, w.block_size)
+    exp = oracle.paged_prefill_attention(case.q, kp, vp, case.block_tables, case.start_pos, case.chunk_lens, w.scale,
+                                         w.block_size, "bf16")
+    dev = _to_dev(case)
+    # The last sequence of "ranked" gets an invalid start: its rows must come out zero.
+    bad = [b for b, s in enumerate(sp) if s < 0]
+    for b in bad:
+        dev["sp"][b] = -5
+        exp[b] = 0.0
+    out = _run(dev, w.scale, split)
+    got = as_f64(out)
+    assert_close(got, exp, *TOL["bf16"], f"prefill order {order} split={split}")
+    for b, n in enumerate(cl):
+        assert not got[b, :, (0 if b in bad else n):].any(), f"rows past chunk_lens[{b}] are not zero"
 
 
 @pytest.mark.parametrize("split", [None, 64])
