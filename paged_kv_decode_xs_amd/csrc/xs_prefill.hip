@@ -129,9 +129,14 @@ __device__ __forceinline__ uint4 mask4(const uint4 v, uint32_t m) {
   return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
 }
 
-// 16-byte piece p of K row t sits at slot p ^ (t % 8): eight consecutive rows read at the same
-// piece hit eight different bank groups.
-__device__ __forceinline__ int k_off(int t, int p, int stride) { return t * stride + 16 * (p ^ (t & 7)); }
+// 16-byte piece p of K row t sits at slot p ^ s(t). The LDS serves a 16-byte access of 16 lanes at a time from its 64 banks: the 16 rows that 16
+// lanes read (or write) at one piece must land on 16 different 16-byte bank groups. With 256-byte
+// rows (D = 128) every row starts at bank 0, so the piece is XORed with t % 16; with 128-byte
+// rows (D = 64) rows t and t + 1 share a bank line, so with (t / 2) % 8.
+template <int D>
+__device__ __forceinline__ int k_off(int t, int p) {
+  return t * (2 * D) + 16 * (p ^ (D == 128 ? (t & 15) : ((t >> 1) & 7)));
+}
 // Score register r of chain h2 and lane half hl holds token 32h2 + 8(r/4) + 4hl + r%4 of the tile.
 // V rows are stored like K rows (token-major, 2D bytes), 16-byte piece p of row t at slot
 // p ^ v_swz(t): eight consecutive rows written at one piece hit eight bank groups, and the four
@@ -420,7 +425,7 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
       for (int r = 0; r < LD::LOADS; ++r) {
         const int u = kWaves * r + wave;
         const int t = 16 * (u & 3) + c, dp = 4 * (u >> 2) + j;
-        *reinterpret_cast<uint4*>(kl + k_off(t, dp, LD::K_STRIDE)) = mask4(R.k[r], R.mask[r]);
+        *reinterpret_cast<uint4*>(kl + k_off<D>(t, dp)) = mask4(R.k[r], R.mask[r]);
         *reinterpret_cast<uint4*>(vl + t * LD::K_STRIDE + 16 * (dp ^ v_swz(t))) = mask4(R.v[r], R.mask[r]);
       }
     };
@@ -433,8 +438,8 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
       float16_t sa0 = {}, sa1 = {};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint4 k0 = *reinterpret_cast<const uint4*>(kl + k_off(n, 2 * ks + hl, LD::K_STRIDE));
-        const uint4 k1 = *reinterpret_cast<const uint4*>(kl + k_off(32 + n, 2 * ks + hl, LD::K_STRIDE));
+        const uint4 k0 = *reinterpret_cast<const uint4*>(kl + k_off<D>(n, 2 * ks + hl));
+        const uint4 k1 = *reinterpret_cast<const uint4*>(kl + k_off<D>(32 + n, 2 * ks + hl));
         sa0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k0), as_bf16x8(qop[ks]), sa0, 0, 0, 0);
         sa1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k1), as_bf16x8(qop[ks]), sa1, 0, 0, 0);
       }
