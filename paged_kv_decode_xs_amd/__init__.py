@@ -32,4 +32,4 @@ from ._binding import (  # noqa: F401
     xs_stream_read_probe,
     xs_version,
 )
-from .step import DecodeStep, StepGraph  # noqa: F401
+from .step import DecodeStep, StepGraph, suggest_partition_size  # noqa: F401

@@ -132,3 +132,30 @@ def test_prefill_case_rejects_bad_ranges():
         make_prefill_case(_tiny_prefill(chunk_lens=(21, 7, 0)))
     with pytest.raises(ValueError):
         make_prefill_case(_tiny_prefill(start_pos=(0, 13, 90)))
+
+
+# Host-side partition-size rule of the decode step helper.
+from paged_kv_decode_xs_amd.step import suggest_partition_size  # noqa: E402
+
+
+def test_suggested_partition_sizes_match_the_measured_best():
+    base = wl.WORKLOADS["qwen3_8b_b64"]
+    for batch, seed, want in ((64, 3, 1024), (128, 5, 2048), (256, 6, 4096)):
+        w = base.with_(batch=batch, seed=seed)
+        lens = wl.make_layout(w, np.random.default_rng(w.seed)).context_lens
+        assert suggest_partition_size(lens, w.num_kv_heads, w.block_size) == want, batch
+    tp = wl.WORKLOADS["qwen3_8b_b64_tp8_share"]
+    lens = wl.make_layout(tp, np.random.default_rng(tp.seed)).context_lens
+    assert suggest_partition_size(lens, tp.num_kv_heads, tp.block_size) == 128
+
+
+def test_suggested_partition_size_edges():
+    assert suggest_partition_size([], 8) == 64
+    assert suggest_partition_size([0, 0], 8) == 64
+    assert suggest_partition_size([10], 8, block_size=32) == 64
+    assert suggest_partition_size([100000] * 64, 8, num_cus=1) >= 100000 // 2  # capped near the longest
+    for bs in (8, 16, 32):
+        p = suggest_partition_size([5000] * 300, 8, block_size=bs)
+        assert p % bs == 0 and p & (p - 1) == 0
+    with pytest.raises(ValueError):
+        suggest_partition_size([1], 0)
