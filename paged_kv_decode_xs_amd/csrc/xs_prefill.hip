@@ -27,7 +27,10 @@
 // Split-K (partition size P > 0): a workgroup takes one piece of P key positions of its row
 // block; a row block with several pieces leaves each row's normalised output over the piece and
 // its (max, sum) in the caller's partials, and the merge kernel combines them per row with the
-// log-sum-exp identity (the same as the decode's partition merge).
+// log-sum-exp identity (the same as the decode's partition merge). The device hands workgroups
+// out in id order as CUs free up, so where the sizes differ and the grid is larger than one
+// workgroup per CU the ids go to the pieces (or row blocks) largest first: longest-first list
+// scheduling.
 // SW instances add the sinks and sliding window of the gpt-oss prefill (same diff,
 // `flash_attention_sinks`: one sink logit per query head that only enlarges the softmax
 // denominator; window_size W > 0 keeps the last W positions up to the query's own). A row at
