@@ -322,6 +322,8 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
   const bool row_valid = row_exists && i_c < nlen;
   const int pos_c = s0 + i_c;  // last key position of this row
   const size_t out_row = ((size_t)b * prm.num_q_heads + h_c) * C + i_c;
+  // The row's sink logit in log2 units, loaded now so that its latency is hidden by the loop.
+  const float sink_l2 = SW && prm.sinks && row_exists ? bf16lo_to_f32(prm.sinks[h_c]) * kLog2e : 0.f;
 
   // Last valid chunk position of the workgroup and of this wavefront.
   const int i_hi_wg = min((min(rho0_wg + kRowsPerGroup, rows_total) - 1) / G, nlen - 1);
@@ -562,15 +564,13 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
 
   const float2 lp = with_other_half(l_part);
   const float l_tot = lp.x + lp.y;
-  if (!row_exists) return;
   // The sink of an unsplit row: e^(sigma - m) more in the denominator (in log2 units; a row with
   // no keys keeps its zeros).
   float den = l_tot;
-  if (SW && prm.sinks && npieces <= 1 && m_run != -INFINITY)
-    den += fast_exp2(bf16lo_to_f32(prm.sinks[h_c]) * kLog2e - m_run);
+  if (SW && prm.sinks && npieces <= 1 && m_run != -INFINITY) den += fast_exp2(sink_l2 - m_run);
   const float inv = row_valid && den > 0.f ? 1.f / den : 0.f;
   // acc[md][r] is O[row n][32md + 8(r/4) + 4hl + r%4]: four runs of 4 values per d block.
-  if (npieces > 1 && row_valid) {
+  if (row_exists && npieces > 1 && row_valid) {
     // A piece of a split row block: this row's output over the piece's keys, and its (m, l)
     // (m = -inf, l = 0 and a zero output for a row with no keys in the piece).
     const size_t prow = out_row * prm.max_partitions + piece;
@@ -584,17 +584,36 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
       }
     }
     if (hl == 0) prm.part_ml[prow] = make_float2(m_run, l_tot);
-    return;
   }
-  if (piece > 0) return;  // rows past chunk_lens get their zeros from piece 0
-  uint2* orow = reinterpret_cast<uint2*>(prm.out + out_row * ND);
+  if (piece > 0) return;  // rows past chunk_lens get their zeros from piece 0 (uniform: the whole workgroup)
+  // Output rows. A lane's row is one head of one chunk position, and the rows of a wavefront
+  // belong to several heads, whose rows lie C * D * 2 bytes apart in `out`: written straight from
+  // the accumulators, every store would scatter 16-byte pieces over 32 rows. The bf16 rows are
+  // staged in LDS instead (the tile buffers are free once every wavefront is past its last tile;
+  // 256 rows of 2D bytes fill them exactly, laid out like K rows), then written with ND
+  // consecutive lanes per row, whole rows of 128 or 256 bytes.
+  __syncthreads();
+  if (row_exists) {
+    const int lr = wave * kRowsPerWave + n;
 #pragma unroll
-  for (int md = 0; md < MD; ++md) {
+    for (int md = 0; md < MD; ++md) {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const float* o = reinterpret_cast<const float*>(&acc[md]) + 4 * q4;
-      orow[8 * md + 2 * q4 + hl] = make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float* o = reinterpret_cast<const float*>(&acc[md]) + 4 * q4;
+        *reinterpret_cast<uint2*>(lds + k_off<D>(lr, 4 * md + q4) + 8 * hl) =
+            make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
+      }
     }
+  }
+  __syncthreads();
+  const int nrows = min(kRowsPerGroup, rows_total - rho0_wg);
+  for (int x = tid; x < nrows * ND; x += 64 * kWaves) {
+    const int lr = x / ND, p = x % ND;
+    const int rho = rho0_wg + lr;
+    const int i = rho / G;
+    if (npieces > 1 && i < nlen) continue;  // split rows: the merge writes them
+    const size_t orow = ((size_t)b * prm.num_q_heads + g * G + rho % G) * C + i;
+    prm.out[orow * ND + p] = *reinterpret_cast<const uint4*>(lds + k_off<D>(lr, p));
   }
 }
 
