@@ -438,8 +438,9 @@ PREFILL_ROWS = {"chunked_prefill": "qwen3_8b_prefill_c512", "chunked_prefill_lon
 
 def prefill_row(name: str = "qwen3_8b_prefill_c512", reps: int = 20, partitions=None) -> dict:
     """Chunked prefill on the Qwen3-8B shape: the multi-token append and the causal attention of
-    the chunk, each timed alone (HIP events on the launch stream, median of `reps`: around one
-    attention call, around 20 back-to-back append launches). The attention is timed whole
+    the chunk, each timed alone (HIP events on the launch stream, median of `reps` event pairs,
+    each around 10 back-to-back attention calls or 20 back-to-back append launches: an event pair
+    around a single call adds a few microseconds to it). The attention is timed whole
     (xs_paged_attn_prefill) and with split-K over the key range (xs_paged_attn_prefill_split: the
     attention kernel and the merge kernel) at the partition sizes of PREFILL_SPLITS; the roofline
     object is the fastest of them. It is a dense contraction on the matrix cores: algorithmic flops
@@ -498,18 +499,24 @@ def prefill_row(name: str = "qwen3_8b_prefill_c512", reps: int = 20, partitions=
         for _ in range(20):
             xs.xs_kv_append_chunk(ks, vs, kc, vc, bt, sp, cl, stream=stream)
     append_ms = med(append20) / 20
+
+    def times10(fn):
+        def run():
+            for _ in range(10):
+                fn()
+        return run
     paths = [0, *PREFILL_SPLITS.get(name, ())] if partitions is None else list(partitions)
     by_p = {}
     finite = True
     if 0 in paths:
-        by_p[0] = med(lambda: attend(0, out))
+        by_p[0] = med(times10(lambda: attend(0, out))) / 10
         finite = bool(torch.isfinite(out.float()).all().item())
     for P in (p for p in paths if p):
         NP = xs.num_partitions(bt.shape[1] * kc.shape[2], P)
         po = torch.empty((*q.shape[:3], NP, q.shape[3]), dtype=torch.float32, device="cuda")
         pml = torch.empty((*q.shape[:3], NP, 2), dtype=torch.float32, device="cuda")
         out_s = torch.empty_like(q)
-        by_p[P] = med(lambda: attend(P, out_s, po, pml))
+        by_p[P] = med(times10(lambda: attend(P, out_s, po, pml))) / 10
         finite = finite and bool(torch.isfinite(out_s.float()).all().item())
         del po, pml, out_s
     best_p = min(by_p, key=by_p.get)
