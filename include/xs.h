@@ -102,7 +102,8 @@ int xs_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_ca
  *     part_o[b, h, j, :]  = sum_t exp(s_t - m_j) V_t / l_j           [batch, num_q_heads, NP, head_dim]
  *   with NP = max_partitions. `out` is not touched (it may be NULL); xs_paged_attn_reduce
  *   produces it. Entries j >= n_b are not written. Partitions at j >= max_partitions are
- *   not computed, so the caller must give max_partitions >= max_b ceil(L_b / P).
+ *   not computed, so the caller must give max_partitions >= max_b ceil(L_b / P); the reduce
+ *   writes NaN rows for a sequence where that does not hold.
  */
 int xs_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_tables, const int32_t* context_lens,
@@ -256,8 +257,11 @@ int xs_step_graph_destroy(xs_step_graph* graph);
  * unsplit softmax). For each (b, h), with n = min(ceil(L_b / P), max_partitions),
  *   M = max_j m_j,  w_j = l_j exp(m_j - M),  out[b, h, :] = sum_j w_j o_j / sum_j w_j.
  * Reads part_o/part_m/part_l as written by xs_paged_attn_decode with the same partition_size
- * and max_partitions. Writes out [batch, num_q_heads, head_dim] in `dtype`. L_b <= 0, or a
- * sequence whose partitions all have l_j = 0, gives zeros.
+ * and max_partitions (part_o and out 16-byte aligned). Writes out [batch, num_q_heads, head_dim]
+ * in `dtype`. L_b <= 0, or a
+ * sequence whose partitions all have l_j = 0, gives zeros. A sequence with ceil(L_b / P) >
+ * max_partitions (the decode did not compute its last partitions) gives NaN rows, so that a
+ * truncated context cannot pass for a result.
  */
 int xs_paged_attn_reduce(const float* part_o, const float* part_m, const float* part_l,
                          const int32_t* context_lens, void* out,

@@ -239,6 +239,7 @@ XS_API int xs_paged_attn_reduce_sinks(const float* part_o, const float* part_m, 
   if (batch == 0) return ok();
   if (!part_o || !part_m || !part_l || !context_lens || !out)
     return fail(XS_EINVAL, "%s: a required pointer is NULL", who);
+  if (!aligned16(part_o) || !aligned16(out)) return fail(XS_EINVAL, "%s: part_o and out must be 16-byte aligned", who);
   if (sinks && (reinterpret_cast<uintptr_t>(sinks) & 1u)) return fail(XS_EINVAL, "%s: sinks must be 2-byte aligned", who);
   (void)hipGetLastError();
   return launch_status(who, xs::launch_paged_reduce_sinks(part_o, part_m, part_l, context_lens, sinks, window_size, out,
@@ -261,6 +262,7 @@ XS_API int xs_paged_attn_reduce(const float* part_o, const float* part_m, const 
   if (batch == 0) return ok();
   if (!part_o || !part_m || !part_l || !context_lens || !out)
     return fail(XS_EINVAL, "%s: a required pointer is NULL", who);
+  if (!aligned16(part_o) || !aligned16(out)) return fail(XS_EINVAL, "%s: part_o and out must be 16-byte aligned", who);
   (void)hipGetLastError();
   return launch_status(who, xs::launch_paged_reduce(part_o, part_m, part_l, context_lens, out, batch, num_q_heads,
                                                     head_dim, partition_size, max_partitions, dtype == XS_BF16,

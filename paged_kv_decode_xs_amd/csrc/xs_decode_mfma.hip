@@ -37,6 +37,15 @@ constexpr int decode_smem_bytes() {
   return NW * TA::STAGE_BYTES > (NW - 1) * MERGE_FLOATS * 4 ? NW * TA::STAGE_BYTES : (NW - 1) * MERGE_FLOATS * 4;
 }
 
+// Writes zeros to rows q_row0 .. q_row0+GC-1 of out (one wavefront, 16 bytes per lane and store).
+template <int D, int GC>
+__device__ __forceinline__ void zero_rows(void* out, size_t q_row0, int lane) {
+  constexpr int PIECES = GC * (D / 8);  // 16-byte pieces
+  uint4* o = reinterpret_cast<uint4*>(out) + q_row0 * (D / 8);
+#pragma unroll
+  for (int i = lane; i < PIECES; i += 64) o[i] = make_uint4(0, 0, 0, 0);
+}
+
 // One work item: partition p of (sequence b, kv head g, head chunk ch).
 template <int D, int BS, int GC, int NW, bool SW>
 __device__ __forceinline__ void decode_item(const DecodeParams& prm, unsigned char* smem, const int p, const int b,
@@ -57,26 +66,28 @@ __device__ __forceinline__ void decode_item(const DecodeParams& prm, unsigned ch
   const int max_partitions = prm.max_partitions;
   const bool split = prm.part_blocks > 0;
   const int h0 = g * prm.group + ch * GC;
+  const int32_t* bt = prm.block_tables + (size_t)b * max_blocks_per_seq;
 
+  // The ids of the item's first 64 blocks do not depend on the context length (without a window),
+  // so their load goes out together with the length's instead of after it.
+  const int jb0 = split ? p * prm.part_blocks : 0;
+  int ids_pre = -1;
+  if constexpr (!SW) {
+    if (jb0 + lane < max_blocks_per_seq) ids_pre = bt[jb0 + lane];
+  }
   const int L_in = prm.context_lens[b];
   const int L = min(L_in, max_blocks_per_seq * BS);
   const int nblk_seq = L > 0 ? (L + BS - 1) / BS : 0;
-  int jb = 0, je = nblk_seq;
+  int jb = jb0, je = split ? min(jb0 + prm.part_blocks, nblk_seq) : nblk_seq;
   // First position in the window (0 without one); blocks wholly before it are skipped.
   const int t0w = SW && prm.window > 0 ? max(0, L - prm.window) : 0;
-  if (split) {
-    jb = p * prm.part_blocks;
-    je = min(jb + prm.part_blocks, nblk_seq);
-  }
   if constexpr (SW) jb = max(jb, t0w / BS);
   if (split && jb >= je) return;  // the whole workgroup leaves together
   const size_t q_row0 = (size_t)b * prm.num_q_heads + h0;
   if (jb >= je) {  // no split, empty context
-    if (wave == 0 && lane < GC * ROW16)
-      reinterpret_cast<uint4*>(prm.out)[q_row0 * ROW16 + lane] = make_uint4(0, 0, 0, 0);
+    if (wave == 0) zero_rows<D, GC>(prm.out, q_row0, lane);
     return;
   }
-  const int32_t* bt = prm.block_tables + (size_t)b * max_blocks_per_seq;
   auto valid = [&](int blk) { return blk >= 0 && blk < prm.num_blocks; };
 
   // Fused append: token L-1 comes from k_new/v_new; the item holding it writes them to the pools.
@@ -106,6 +117,10 @@ __device__ __forceinline__ void decode_item(const DecodeParams& prm, unsigned ch
 
   // Block ids of 64 consecutive blocks of the range sit in one VGPR, one per lane.
   int id_chunk = -1, ids = -1;
+  if constexpr (!SW) {
+    id_chunk = 0;
+    ids = jb + lane < je ? ids_pre : -1;
+  }
   auto block_of = [&](int tile) -> int {
     const int rel = tile / TPB - jb;
     const int c64 = rel >> 6;
@@ -349,12 +364,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(XS_DECO
 void paged_decode_mfma_kernel(const DecodeParams prm) {
   __shared__ __align__(16) unsigned char smem[decode_smem_bytes<D, BS, GC, NW>()];
   int b, p, seg;
-  if (prm.part_blocks > 0 && prm.batch <= kDenseMaxBatch) {
+  if (prm.part_blocks > 0 && prm.batch > 1 && prm.batch <= kDenseMaxBatch) {
     dense_item<BS>(prm, blockIdx.x, b, p, seg);
     if (b < 0) return;  // past the items that exist
   } else if (prm.part_blocks > 0) {
-    // Large batches: partition-major ids (every workgroup would otherwise scan all lengths).
-    // Neighbouring ids then carry similar work, and every XCD gets each partition depth.
+    // Partition-major ids: for one sequence (the ranked order would list its partitions in this
+    // same order, but only after reading its length) and for large batches (where every
+    // workgroup would otherwise scan all lengths). Neighbouring ids carry similar work, and every
+    // XCD gets each partition depth.
     const int per_p = prm.batch * prm.num_kv_heads * prm.chunks;
     p = blockIdx.x / per_p;
     seg = blockIdx.x % (prm.chunks * prm.num_kv_heads);

@@ -1,10 +1,21 @@
-// Log-sum-exp merge of split-K partitions: one wavefront per (sequence, query head).
+// Log-sum-exp merge of split-K partitions: one workgroup per (sequence, query head).
 //
 // Partition j holds (o_j, m_j, l_j) with m_j the max scaled score, l_j = sum exp(s - m_j) and
 // o_j the partition's normalised output. With M = max_j m_j and w_j = l_j exp(m_j - M),
 //   out = sum_j w_j o_j / sum_j w_j,
 // which equals the softmax over the whole context (the partitions split its sum). The split
 // and its merge are this library's design for long contexts; the pages have no split.
+//
+// The merge is a chain of dependent memory round trips (the length, then the partials), so the
+// kernel is built to need as few as it can: every partial of a row is requested in one round.
+// A row of D floats is read by D/4 lanes (16 bytes each), so a wavefront holds S = 256/D rows
+// ("slots") per load; NW wavefronts of a workgroup hold 8 loads each in flight, i.e. 8 * S * NW
+// partitions per round (64 for D = 128 and NW = 4). Each slot folds its partitions into a running
+// (m, l, o) with the same rule, o kept normalised:
+//   m' = max(m, m_j),  a = l e^(m-m'),  c = l_j e^(m_j-m'),  l' = a + c,  o' = (a o + c o_j) / l',
+// then the slots and the wavefronts fold their states together (shuffles, then LDS). Without a
+// window the first round's loads go out before the length arrives (they stay inside the row's
+// max_partitions slots; those past the row's partition count are discarded, never multiplied).
 #include <math.h>
 
 #include "xs_device.h"
@@ -13,191 +24,179 @@
 namespace xs {
 namespace {
 
-template <bool BF16, int D>
-__global__ __launch_bounds__(64) void paged_reduce_kernel(const float* __restrict__ part_o,
-                                                          const float* __restrict__ part_m,
-                                                          const float* __restrict__ part_l,
-                                                          const int32_t* __restrict__ context_lens,
-                                                          void* __restrict__ out, int num_q_heads,
-                                                          int partition_size, int max_partitions) {
-  constexpr int DPL = D / 64;  // output elements per lane
-  constexpr int PRE = 8;       // partitions whose o is fetched before the count is known
-  const int lane = threadIdx.x;
-  const size_t row = blockIdx.x;  // (b, h)
-  const int b = (int)(row / num_q_heads);
-  const float* pm = part_m + row * max_partitions;
-  const float* pl = part_l + row * max_partitions;
-  const float* po = part_o + row * max_partitions * D + (size_t)lane * DPL;
+constexpr int kRedU = 8;  // loads in flight per lane and round
 
-  // Loads that do not depend on L go out together with it: (m, l) of the first 64 slots and o of
-  // the first PRE slots, all inside this row's max_partitions slots. Slots at or past the
-  // partition count n are ignored below.
-  const int L = context_lens[b];
-  float mj = lane < max_partitions ? pm[lane] : -INFINITY;
-  float lj = lane < max_partitions ? pl[lane] : 0.f;
-  float opre[PRE][DPL];
-#pragma unroll
-  for (int u = 0; u < PRE; ++u) {
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) opre[u][e] = u < max_partitions ? po[(size_t)u * D + e] : 0.f;
-  }
-  int n = L > 0 ? (L + partition_size - 1) / partition_size : 0;
-  n = min(n, max_partitions);
-  if (lane >= n) {
-    mj = -INFINITY;
-    lj = 0.f;
-  }
+struct LseState {
+  float m, l;
+  float4 o;
+};
 
-  float M = mj;
-  for (int j = lane + 64; j < n; j += 64) M = fmaxf(M, pm[j]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+__device__ __forceinline__ void lse_fold(LseState& s, float m2, float l2, const float4& o2) {
+  const float mn = fmaxf(s.m, m2);
+  const float ms = mn == -INFINITY ? 0.f : mn;
+  const float a = s.m == -INFINITY ? 0.f : fast_exp2((s.m - ms) * kLog2e) * s.l;
+  const float c = m2 == -INFINITY ? 0.f : fast_exp2((m2 - ms) * kLog2e) * l2;
+  const float ln = a + c;
+  const float inv = ln > 0.f ? 1.f / ln : 0.f;
+  s.o.x = (s.o.x * a + o2.x * c) * inv;
+  s.o.y = (s.o.y * a + o2.y * c) * inv;
+  s.o.z = (s.o.z * a + o2.z * c) * inv;
+  s.o.w = (s.o.w * a + o2.w * c) * inv;
+  s.m = mn;
+  s.l = ln;
+}
 
-  float acc[DPL];
+// One round: the slot's partitions j = base + k * stride, k < kRedU, folded in if j0 <= j < n.
+template <int D>
+__device__ __forceinline__ void fold_round(LseState& st, const float* pm, const float* pl, const float4* po, int base,
+                                           int stride, int j0, int n, int maxp) {
+  constexpr int LPR = D / 4;
+  float4 o[kRedU];
+  float m[kRedU], l[kRedU];
 #pragma unroll
-  for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
-  float W = 0.f;
-  if (M != -INFINITY) {
-    const float M2 = M * kLog2e;
-    for (int base = 0; base < n; base += 64) {
-      const int jj = base + lane;
-      float w = 0.f;
-      if (jj < n) w = base == 0 ? lj * fast_exp2(fmaf(mj, kLog2e, -M2)) : pl[jj] * fast_exp2(fmaf(pm[jj], kLog2e, -M2));
-      W += w;
-      const int cnt = min(64, n - base);
-      int k = 0;
-      if (base == 0) {
-#pragma unroll
-        for (int u = 0; u < PRE; ++u) {
-          if (u < cnt) {
-            const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) acc[e] = fmaf(wk, opre[u][e], acc[e]);
-          }
-        }
-        k = PRE;
-      }
-      // Eight partitions per round so that their loads are in flight together.
-      for (; k + 8 <= cnt; k += 8) {
-        float o[8][DPL];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) o[u][e] = po[(size_t)(base + k + u) * D + e];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k + u));
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) acc[e] = fmaf(wk, o[u][e], acc[e]);
-        }
-      }
-      for (; k < cnt; ++k) {
-        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[e] = fmaf(wk, po[(size_t)(base + k) * D + e], acc[e]);
-      }
-    }
+  for (int k = 0; k < kRedU; ++k) {  // every load inside the row's max_partitions slots
+    const int j = min(base + k * stride, maxp - 1);
+    o[k] = po[(size_t)j * LPR];
+    m[k] = pm[j];
+    l[k] = pl[j];
   }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) W += __shfl_xor(W, off, 64);
-  const float inv = W > 0.f ? 1.f / W : 0.f;
-  if constexpr (BF16) {
-    if constexpr (DPL == 2) {
-      reinterpret_cast<uint32_t*>(out)[row * (D / 2) + lane] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    } else {
-      reinterpret_cast<uint16_t*>(out)[row * D + lane] = (uint16_t)f32_to_bf16_rne(acc[0] * inv);
-    }
-  } else {
-    float* o = reinterpret_cast<float*>(out) + row * D + (size_t)lane * DPL;
-#pragma unroll
-    for (int k = 0; k < DPL; ++k) o[k] = acc[k] * inv;
+  for (int k = 0; k < kRedU; ++k) {
+    const int j = base + k * stride;
+    if (j >= j0 && j < n) lse_fold(st, m[k], l[k], o[k]);
   }
 }
 
-
-// The merge with attention sinks and a sliding window (xserv compare phase10...cf1e9e41,
-// attention.rs, `paged_decode_attention_sinks`). The window keeps positions from
-// t0 = max(0, L - window); partitions j < t0 / P hold none of them and were never written.
-// Head h's sink sigma joins the denominator once:
+// SW: per-head sinks and a sliding window (xserv compare phase10...cf1e9e41, attention.rs,
+// `paged_decode_attention_sinks`): partitions before the window start t0 = max(0, L - window)
+// hold no kept position and were never written; head h's sink sigma joins the denominator once:
 //   M = max(sigma, max_j m_j),  out = sum_j l_j e^(m_j - M) o_j / (e^(sigma - M) + sum_j l_j e^(m_j - M)).
-template <bool BF16, int D>
-__global__ __launch_bounds__(64) void paged_reduce_sinks_kernel(const float* __restrict__ part_o,
-                                                                const float* __restrict__ part_m,
-                                                                const float* __restrict__ part_l,
-                                                                const int32_t* __restrict__ context_lens,
-                                                                const uint16_t* __restrict__ sinks, int window,
-                                                                void* __restrict__ out, int num_q_heads,
-                                                                int partition_size, int max_partitions) {
-  constexpr int DPL = D / 64;  // output elements per lane
-  const int lane = threadIdx.x;
+template <bool BF16, int D, int NW, bool SW>
+__global__ __launch_bounds__(64 * NW) void paged_reduce_kernel(const float* __restrict__ part_o,
+                                                               const float* __restrict__ part_m,
+                                                               const float* __restrict__ part_l,
+                                                               const int32_t* __restrict__ context_lens,
+                                                               const uint16_t* __restrict__ sinks, int window,
+                                                               void* __restrict__ out, int num_q_heads,
+                                                               int partition_size, int max_partitions) {
+  constexpr int LPR = D / 4;   // lanes per partial row
+  constexpr int S = 64 / LPR;  // slots per wavefront
+  __shared__ __align__(16) float lds[(NW > 1 ? NW - 1 : 1) * (2 + 4) * LPR];
+  const int wave = NW > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
+  const int lane = threadIdx.x & 63;
+  const int slot = lane / LPR, c = lane % LPR;
   const size_t row = blockIdx.x;  // (b, h)
   const int b = (int)(row / num_q_heads);
-  const int h = (int)(row % num_q_heads);
-  const float* pm = part_m + row * max_partitions;
-  const float* pl = part_l + row * max_partitions;
-  const float* po = part_o + row * max_partitions * D + (size_t)lane * DPL;
+  const int maxp = max_partitions;
+  const float* pm = part_m + row * maxp;
+  const float* pl = part_l + row * maxp;
+  const float4* po = reinterpret_cast<const float4*>(part_o + row * maxp * D) + c;
+  const int stride = S * NW;           // between a slot's consecutive partitions
+  const int first = wave * S + slot;   // the slot's first partition
+  const int per_round = stride * kRedU;
 
+  LseState st{-INFINITY, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
   const int L = context_lens[b];
-  const int t0 = window > 0 ? max(0, L - window) : 0;
-  const int j0 = L > 0 ? t0 / partition_size : 0;
-  const int n = L > 0 ? min((L + partition_size - 1) / partition_size, max_partitions) : 0;
-  const float sig = sinks ? __uint_as_float((uint32_t)sinks[h] << 16) : -INFINITY;
-
-  float M = -INFINITY;
-  for (int j = j0 + lane; j < n; j += 64) M = fmaxf(M, pm[j]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-  M = fmaxf(M, sig);
-
-  float acc[DPL];
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-  float W = 0.f;
-  if (n > j0 && M != -INFINITY) {
-    const float M2 = M * kLog2e;
-    for (int base = j0; base < n; base += 64) {
-      const int jj = base + lane;
-      const float w = jj < n ? pl[jj] * fast_exp2(fmaf(pm[jj], kLog2e, -M2)) : 0.f;
-      W += w;
-      const int cnt = min(64, n - base);
-      int k = 0;
-      for (; k + 8 <= cnt; k += 8) {  // eight partitions' o in flight together
-        float o[8][DPL];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) o[u][e] = po[(size_t)(base + k + u) * D + e];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k + u));
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) acc[e] = fmaf(wk, o[u][e], acc[e]);
-        }
-      }
-      for (; k < cnt; ++k) {
-        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[e] = fmaf(wk, po[(size_t)(base + k) * D + e], acc[e]);
-      }
-    }
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) W += __shfl_xor(W, off, 64);
-  if (n > j0 && sig != -INFINITY) W += fast_exp2((sig - M) * kLog2e);
-  const float inv = W > 0.f ? 1.f / W : 0.f;
-  if constexpr (BF16) {
-    if constexpr (DPL == 2) {
-      reinterpret_cast<uint32_t*>(out)[row * (D / 2) + lane] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    } else {
-      reinterpret_cast<uint16_t*>(out)[row * D + lane] = (uint16_t)f32_to_bf16_rne(acc[0] * inv);
-    }
+  const int n_all = L > 0 ? (L + partition_size - 1) / partition_size : 0;
+  const bool overflow = n_all > maxp;  // partitions were cut: the output is NaN
+  const int n = min(n_all, maxp);
+  int j0 = 0;
+  if constexpr (SW) {
+    j0 = (L > 0 && window > 0 ? max(0, L - window) : 0) / partition_size;
+    for (int base = j0 - j0 % per_round + first; base - first < n; base += per_round)
+      fold_round<D>(st, pm, pl, po, base, stride, j0, n, maxp);
   } else {
-    float* o = reinterpret_cast<float*>(out) + row * D + (size_t)lane * DPL;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) o[e] = acc[e] * inv;
+    // Round 0 is issued with the length load (before n is known).
+    fold_round<D>(st, pm, pl, po, first, stride, 0, n, maxp);
+    for (int base = first + per_round; base - first < n; base += per_round)
+      fold_round<D>(st, pm, pl, po, base, stride, 0, n, maxp);
   }
+  // Fold the slots of the wavefront, then the wavefronts.
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+    const float4 o2 = make_float4(__shfl_xor(st.o.x, off, 64), __shfl_xor(st.o.y, off, 64),
+                                  __shfl_xor(st.o.z, off, 64), __shfl_xor(st.o.w, off, 64));
+    lse_fold(st, __shfl_xor(st.m, off, 64), __shfl_xor(st.l, off, 64), o2);
+  }
+  if constexpr (NW > 1) {
+    if (wave > 0 && slot == 0) {
+      float* mine = lds + (wave - 1) * 6 * LPR;
+      mine[c] = st.m;
+      mine[LPR + c] = st.l;
+      reinterpret_cast<float4*>(mine + 2 * LPR)[c] = st.o;
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      const float* other = lds + (w - 1) * 6 * LPR;
+      lse_fold(st, other[c], other[LPR + c], reinterpret_cast<const float4*>(other + 2 * LPR)[c]);
+    }
+  }
+  float f = 1.f;
+  if (SW && sinks && n > j0) {
+    const float sg = __uint_as_float((uint32_t)sinks[row % num_q_heads] << 16);
+    const float M = fmaxf(st.m, sg);
+    const float a = st.m == -INFINITY ? 0.f : fast_exp2((st.m - M) * kLog2e) * st.l;
+    const float den = a + (sg == -INFINITY ? 0.f : fast_exp2((sg - M) * kLog2e));
+    f = den > 0.f ? a / den : 0.f;
+  }
+  if (overflow) f = NAN;
+  if (slot != 0) return;
+  const float4 v = make_float4(st.o.x * f, st.o.y * f, st.o.z * f, st.o.w * f);
+  if constexpr (BF16) {
+    reinterpret_cast<uint2*>(out)[row * LPR + c] = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+  } else {
+    reinterpret_cast<float4*>(out)[row * LPR + c] = v;
+  }
+}
+
+// Wavefronts per row: enough that one round covers max_partitions, at most 4.
+int reduce_waves(int head_dim, int max_partitions) {
+  const int per_wave = kRedU * (256 / head_dim);
+  return max_partitions <= per_wave ? 1 : max_partitions <= 2 * per_wave ? 2 : 4;
+}
+
+template <bool BF16, int D, bool SW>
+hipError_t launch_rows(const float* part_o, const float* part_m, const float* part_l, const int32_t* context_lens,
+                       const void* sinks, int window, void* out, int batch, int num_q_heads, int partition_size,
+                       int max_partitions, hipStream_t stream) {
+  const dim3 grid((unsigned)((long long)batch * num_q_heads));
+  const uint16_t* sk = static_cast<const uint16_t*>(sinks);
+  switch (reduce_waves(D, max_partitions)) {
+    case 1:
+      hipLaunchKernelGGL((paged_reduce_kernel<BF16, D, 1, SW>), grid, dim3(64), 0, stream, part_o, part_m, part_l,
+                         context_lens, sk, window, out, num_q_heads, partition_size, max_partitions);
+      break;
+    case 2:
+      hipLaunchKernelGGL((paged_reduce_kernel<BF16, D, 2, SW>), grid, dim3(128), 0, stream, part_o, part_m, part_l,
+                         context_lens, sk, window, out, num_q_heads, partition_size, max_partitions);
+      break;
+    default:
+      hipLaunchKernelGGL((paged_reduce_kernel<BF16, D, 4, SW>), grid, dim3(256), 0, stream, part_o, part_m, part_l,
+                         context_lens, sk, window, out, num_q_heads, partition_size, max_partitions);
+      break;
+  }
+  return hipGetLastError();
+}
+
+template <bool SW>
+hipError_t launch_any(const float* part_o, const float* part_m, const float* part_l, const int32_t* context_lens,
+                      const void* sinks, int window, void* out, int batch, int num_q_heads, int head_dim,
+                      int partition_size, int max_partitions, bool bf16, hipStream_t stream) {
+  if (bf16 && head_dim == 64)
+    return launch_rows<true, 64, SW>(part_o, part_m, part_l, context_lens, sinks, window, out, batch, num_q_heads,
+                                     partition_size, max_partitions, stream);
+  if (bf16 && head_dim == 128)
+    return launch_rows<true, 128, SW>(part_o, part_m, part_l, context_lens, sinks, window, out, batch, num_q_heads,
+                                      partition_size, max_partitions, stream);
+  if (!bf16 && head_dim == 64)
+    return launch_rows<false, 64, SW>(part_o, part_m, part_l, context_lens, sinks, window, out, batch, num_q_heads,
+                                      partition_size, max_partitions, stream);
+  if (!bf16 && head_dim == 128)
+    return launch_rows<false, 128, SW>(part_o, part_m, part_l, context_lens, sinks, window, out, batch, num_q_heads,
+                                       partition_size, max_partitions, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -205,43 +204,16 @@ __global__ __launch_bounds__(64) void paged_reduce_sinks_kernel(const float* __r
 hipError_t launch_paged_reduce(const float* part_o, const float* part_m, const float* part_l,
                                const int32_t* context_lens, void* out, int batch, int num_q_heads, int head_dim,
                                int partition_size, int max_partitions, bool bf16, hipStream_t stream) {
-  const dim3 grid((unsigned)((long long)batch * num_q_heads));
-#define XS_LAUNCH(BF, D_)                                                                                      \
-  hipLaunchKernelGGL((paged_reduce_kernel<BF, D_>), grid, dim3(64), 0, stream, part_o, part_m, part_l,       \
-                     context_lens, out, num_q_heads, partition_size, max_partitions)
-  if (bf16) {
-    if (head_dim == 64) XS_LAUNCH(true, 64);
-    else if (head_dim == 128) XS_LAUNCH(true, 128);
-    else return hipErrorInvalidValue;
-  } else {
-    if (head_dim == 64) XS_LAUNCH(false, 64);
-    else if (head_dim == 128) XS_LAUNCH(false, 128);
-    else return hipErrorInvalidValue;
-  }
-#undef XS_LAUNCH
-  return hipGetLastError();
+  return launch_any<false>(part_o, part_m, part_l, context_lens, nullptr, 0, out, batch, num_q_heads, head_dim,
+                           partition_size, max_partitions, bf16, stream);
 }
 
 hipError_t launch_paged_reduce_sinks(const float* part_o, const float* part_m, const float* part_l,
                                      const int32_t* context_lens, const void* sinks, int window, void* out,
                                      int batch, int num_q_heads, int head_dim, int partition_size,
                                      int max_partitions, bool bf16, hipStream_t stream) {
-  const dim3 grid((unsigned)((long long)batch * num_q_heads));
-  const uint16_t* sk = static_cast<const uint16_t*>(sinks);
-#define XS_LAUNCH(BF, D_)                                                                                        \
-  hipLaunchKernelGGL((paged_reduce_sinks_kernel<BF, D_>), grid, dim3(64), 0, stream, part_o, part_m, part_l,    \
-                     context_lens, sk, window, out, num_q_heads, partition_size, max_partitions)
-  if (bf16) {
-    if (head_dim == 64) XS_LAUNCH(true, 64);
-    else if (head_dim == 128) XS_LAUNCH(true, 128);
-    else return hipErrorInvalidValue;
-  } else {
-    if (head_dim == 64) XS_LAUNCH(false, 64);
-    else if (head_dim == 128) XS_LAUNCH(false, 128);
-    else return hipErrorInvalidValue;
-  }
-#undef XS_LAUNCH
-  return hipGetLastError();
+  return launch_any<true>(part_o, part_m, part_l, context_lens, sinks, window, out, batch, num_q_heads, head_dim,
+                          partition_size, max_partitions, bf16, stream);
 }
 
 }  // namespace xs

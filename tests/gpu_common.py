@@ -63,9 +63,18 @@ def run_step(dev: Dict[str, torch.Tensor], scale: float, partition_size: int, ma
     step = xs.DecodeStep(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["context_lens"],
                          dev["k_new"], dev["v_new"], scale, partition_size=partition_size,
                          max_context_len=max_context_len, fused=fused, schedule=schedule)
+    nan_fill(step)
     step.run()
     torch.cuda.synchronize()
     return step
+
+
+def nan_fill(step) -> None:
+    """Poison a step's output and partials, so that anything the kernels leave unwritten shows."""
+    for t in (step.out, step.part_o, step.part_m, step.part_l):
+        if t is not None:
+            t.fill_(float("nan"))
+
 
 
 def check_case(case, partition_size: int, ref: OracleResult = None, check_pools: bool = True, label: str = "",
@@ -91,6 +100,7 @@ def check_case(case, partition_size: int, ref: OracleResult = None, check_pools:
 
 
 def check_partials(step, ref: OracleResult, case) -> None:
+    """GPU partials against the oracle's partition statistics."""
     po = step.part_o.cpu().double().numpy()
     pm = step.part_m.cpu().double().numpy()
     pl = step.part_l.cpu().double().numpy()
