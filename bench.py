@@ -1,28 +1,37 @@
 """Decode-step benchmark on one MI355X: KV append + split-K paged decode attention + LSE reduce.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--partition P] [--copies R]
+    python bench.py [--steps K] [--warmup W] [--only WORKLOAD] [--copies R]
 
-Prints ONE JSON line on stdout (diagnostics go to stderr):
+Prints ONE JSON line on stdout (diagnostics go to stderr). The headline is the 64-sequence
+Qwen3-8B batch; every other decode workload gets a row of its own.
   value         K+V bytes the step must stream / measured step time, in GB/s (whole job, 1 GPU)
   ms_per_step   mean time of one step on the GPU (HIP events around K back-to-back steps)
   seqs_per_s    batch / step time
-  roofline      the decode kernel alone: its algorithmic bytes per launch / its mean duration
-                (HIP events around each decode launch, on the launch stream, in a second pass
-                of the same K steps) vs 8 TB/s;
+  roofline      the decode kernel alone: its algorithmic bytes per launch / its mean duration,
+                which is one HIP event pair around K back-to-back decode launches (the fused
+                append + decode call, no reduce) on the launch stream; vs 8 TB/s.
                 `traffic` is the HBM bytes per launch counted by rocprofv3 (FETCH_SIZE and
                 WRITE_SIZE, calibrated on a 1 GiB copy; the summary is committed in profiles/)
                 over the same mean duration, in GB/s like `achieved`; null when the kernel
                 source changed since the counters were taken
-  cpu_baseline  the fp64 oracle timed on the host over a bounded sample of the same workload;
+  configs       one row per decode workload of the specification (GPT-2 fp32 and bf16, Qwen3-8B
+                single stream, the 64-sequence batch, the 4-sequence long context), each
+                cache-defeated: the pools exist in R copies and consecutive steps read different
+                copies, more than 1 GB apart. A row's step time is one HIP event pair around
+                replays of a HIP graph holding one step per pool copy (so host launch overhead
+                does not hide the GPU time of the small steps); its roofline is the step's
+                algorithmic bytes over that time. The 64-sequence row repeats the headline.
+  cpu_baseline  the fp64 oracle timed on the host over a bounded sample of the headline workload;
                 its output is also compared with the GPU's for those sequences
   self_checks   block-permutation invariance (bitwise) and a length-1 sequence returning its V row
                 exactly, run on every bench run; a failure makes the exit status 3
-  extra rows    other decode workloads, KV block swap, chunked prefill (its own MFMA roofline),
-                and HIP-graph replay (see the functions below)
+  extra rows    the one-GPU share at tensor parallelism 8 and the gpt-oss windowed layer (as
+                config rows), KV block swap, chunked prefill (its own MFMA roofline), and HIP-graph
+                replay of layer stacks (warm)
 
-Inputs are generated once and resident in HBM before timing. The pools exist in R copies
-(default: enough that R x pool > 3 GB), and step k reads copy k % R. Each step therefore
-streams K/V that no recent step touched, and the 256 MB Infinity Cache cannot serve it.
+Inputs are generated once and resident in HBM before timing. The headline pools exist in R
+copies (default: enough that R x pool > 3 GB), and step k reads copy k % R, so each step streams
+K/V that no recent step touched and the 256 MB Infinity Cache cannot serve it.
 """
 
 from __future__ import annotations
@@ -44,7 +53,15 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 METRIC = "paged decode attention KV GB/s (% of HBM peak) + seqs/s, Qwen3-8B GQA shape"
 DECODE_SOURCES = ["paged_kv_decode_xs_amd/csrc/xs_decode.hip", "paged_kv_decode_xs_amd/csrc/xs_decode_mfma.hip",
-                  "paged_kv_decode_xs_amd/csrc/xs_mfma_tile.h", "paged_kv_decode_xs_amd/csrc/xs_device.h"]
+                  "paged_kv_decode_xs_amd/csrc/xs_mfma_tile.h", "paged_kv_decode_xs_amd/csrc/xs_device.h",
+                  "paged_kv_decode_xs_amd/csrc/xs_reduce.hip"]
+HEADLINE = "qwen3_8b_b64"
+# The specification's five decode workloads, in its order, with the partition size each step uses
+# (0: unsplit, one launch; the fp32 GPT-2 step is 32 tokens).
+CONFIGS = [("gpt2_fp32_ctx32", 0), ("gpt2_bf16_b8", 128), ("qwen3_8b_b1_ctx4096", 128), ("qwen3_8b_b64", 1024),
+           ("qwen3_8b_b4_long", 512)]
+# Further decode workloads measured like the config rows.
+EXTRA_WORKLOADS = [("qwen3_8b_b64_tp8_share", 256), ("gptoss_20b_window128_b64", 0)]
 
 
 def log(msg: str) -> None:
@@ -59,22 +76,37 @@ def decode_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str, partition: int, fused: bool):
-    """Per-launch HBM bytes of the decode kernel from the committed rocprofv3 counter summary."""
-    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.txt")
-    if not os.path.exists(path):
-        return None
+def _read_summary(path: str) -> dict:
     kv = {}
-    with open(path) as f:
-        for line in f:
-            if ":" in line and not line.startswith("#"):
-                k, v = line.split(":", 1)
-                kv[k.strip()] = v.strip()
-    if (kv.get("decode_source_sha256") != decode_source_hash() or kv.get("partition_size") != str(partition)
-            or kv.get("fused") != str(fused)):
+    if os.path.exists(path):
+        with open(path) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+    return kv
+
+
+def read_traffic(workload: str, partition: int):
+    """HBM bytes per launch of the step's kernels (decode, reduce) from the committed rocprofv3
+    counter summary of this workload, or None when it is missing or was taken on other sources."""
+    kv = _read_summary(os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.txt"))
+    if kv.get("decode_source_sha256") != decode_source_hash() or kv.get("partition_size") != str(partition):
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return {"decode": float(kv["decode_hbm_bytes_per_launch"]),
+                "reduce": float(kv.get("reduce_hbm_bytes_per_launch", "0"))}
+    except (KeyError, ValueError):
+        return None
+
+
+def read_trace(workload: str, partition: int):
+    """Mean kernel durations (us) of the step from the committed rocprofv3 kernel trace, or None."""
+    kv = _read_summary(os.path.join(ROOT, "profiles", f"decode_{workload}_kernel_trace.txt"))
+    if kv.get("decode_source_sha256") != decode_source_hash() or kv.get("partition_size") != str(partition):
+        return None
+    try:
+        return {"decode_us": float(kv["decode_avg_us"]), "reduce_us": float(kv.get("reduce_avg_us", "0"))}
     except (KeyError, ValueError):
         return None
 
@@ -172,13 +204,12 @@ def cpu_baseline(case, gpu_out, budget_s: float):
     }, {"sequences_checked": done, "max_abs_err": max_err, "out_of_tolerance": bad}
 
 
-# Workloads measured after the headline one, each on its own line in "extra_workloads".
-EXTRA_WORKLOADS = ["qwen3_8b_b64_tp8_share", "gptoss_20b_window128_b64"]
 
 
-def run_workload(w, P: int, fused: bool, K: int, warmup: int, copies=None):
-    """Generate, upload and time one workload: K back-to-back steps (no events inside), then the
-    same K steps again with HIP events around each decode launch."""
+def rotated_steps(w, P: int, fused: bool, copies=None, min_apart: float = 1.2e9):
+    """Generate the workload, upload it, and make R pool copies with one DecodeStep each. R is
+    chosen so that R x pool > 3 GB and more than `min_apart` bytes of K+V are read between two
+    uses of one copy: the 256 MB Infinity Cache then holds nothing a step reads."""
     import torch
 
     import paged_kv_decode_xs_amd as xs
@@ -194,69 +225,140 @@ def run_workload(w, P: int, fused: bool, K: int, warmup: int, copies=None):
     if case.sinks is not None:
         sinks = torch.from_numpy(case.sinks.view(np.int16).copy()).view(torch.bfloat16).to("cuda:0")
     pool_bytes = 2 * dev["k_cache"].numel() * dev["k_cache"].element_size()
-    # Enough copies that > 3 GB of pool, and > 768 MB of the bytes a step reads, pass between two
-    # uses of one copy: the 256 MB Infinity Cache then holds none of what a step reads.
-    R = copies or max(2, math.ceil(3e9 / pool_bytes), math.ceil(768e6 / max(case.kv_bytes(), 1)))
-    R = max(1, min(R, int(48e9 // pool_bytes)))
+    R = copies or max(2, math.ceil(3e9 / pool_bytes), math.ceil(min_apart / max(case.kv_bytes(), 1)) + 1)
+    R = max(1, min(R, 4096, int(48e9 // pool_bytes)))
     pools = [(dev["k_cache"], dev["v_cache"])] + [(dev["k_cache"].clone(), dev["v_cache"].clone())
                                                    for _ in range(R - 1)]
     maxlen = int(case.context_lens.max())
     steps = [xs.DecodeStep(dev["q"], kc, vc, dev["block_tables"], dev["context_lens"], dev["k_new"], dev["v_new"],
-                           w.scale, partition_size=P, max_context_len=maxlen, fused=fused, sinks=sinks,
-                           window=w.window) for kc, vc in pools]
+                           w.scale, partition_size=P, max_context_len=maxlen if P else None, fused=fused,
+                           sinks=sinks, window=w.window) for kc, vc in pools]
+    return case, steps
+
+
+def _events():
+    import torch
+
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def time_calls(fn, K: int, stream) -> float:
+    """Mean ms of fn(i) over K back-to-back calls: one HIP event pair on `stream` around them all."""
+    import torch
+
+    a, b = _events()
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(K):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / K
+
+
+def run_headline(w, P: int, fused: bool, K: int, warmup: int, copies=None) -> dict:
+    """The headline workload: K back-to-back steps (append + decode + reduce) on rotated pools;
+    then K back-to-back decode launches alone (the roofline's duration), in groups whose means
+    give the spread; then K steps on one copy (warm-cache reference)."""
+    import torch
+
+    case, steps = rotated_steps(w, P, fused, copies)
+    R = len(steps)
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         steps[i % R].run(stream)
     torch.cuda.synchronize()
 
-    def one_step(i, ev=None):
+    def step(i):
+        steps[i % R].run(stream)
+
+    def decode_only(i):
         s = steps[i % R]
         if fused:
-            if ev is not None:
-                ev[0].record(stream)
             s.append_and_attend(stream)
         else:
-            s.append(stream)
-            if ev is not None:
-                ev[0].record(stream)
             s.attend(stream)
-        if ev is not None:
-            ev[1].record(stream)
-        s.reduce(stream)
 
-    # Timed region: exactly K steps, no other work or events between them.
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ms_step = time_calls(step, K, stream)
+    ms_decode = time_calls(decode_only, K, stream)
+    groups = 5 if K >= 10 else 1
+    per = max(1, K // groups)
+    group_ms = [time_calls(lambda i, g=g: decode_only(g * per + i), per, stream) for g in range(groups)]
+    ms_warm = time_calls(lambda i: steps[0].run(stream), K, stream)
+    # Leave the last copy with a full step's output for the parity check.
+    steps[(K - 1) % R].run(stream)
     torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(K):
-        one_step(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / K
-
-    # The decode kernel alone: the same K steps again, with HIP events around each decode launch on
-    # its stream (events between launches add a few microseconds of GPU time, so they stay out of
-    # the timed region above).
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    for i in range(K):
-        one_step(i, ev[i])
-    torch.cuda.synchronize()
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
-    # Warm-cache reference: the same K steps, all on pool copy 0 (what the Infinity Cache keeps of
-    # it stays there between steps). Secondary to the rotated (cache-flushed) number above.
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(K):
-        one_step(i * R)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_warm = start.elapsed_time(end) / K
-    decode_ms_mean = float(np.mean(launch_ms))
     out = steps[(K - 1) % R].out.float().cpu().double().numpy()
-    del steps, pools, dev
-    return {"case": case, "R": R, "ms_step": ms_step, "decode_ms_mean": decode_ms_mean, "out": out,
-            "ms_step_warm": ms_warm,
-            "launch_us_p10_p50_p90": [round(float(np.percentile(launch_ms, q)) * 1e3, 2) for q in (10, 50, 90)]}
+    del steps
+    torch.cuda.empty_cache()
+    return {"case": case, "R": R, "ms_step": ms_step, "ms_decode": ms_decode, "ms_warm": ms_warm, "out": out,
+            "decode_group_us": [round(g * 1e3, 2) for g in group_ms]}
+
+
+def decode_row(name: str, P: int, K: int, warmup: int, fused: bool = True, headline=None,
+               min_steps: int = 2000) -> dict:
+    """One decode workload, cache-defeated: a HIP graph of one step per pool copy, replayed until
+    at least `min_steps` steps or 0.2 s have run (one event pair around the replays); plus K eager
+    back-to-back steps (host-bound for the small steps). With `headline` (run_headline's result)
+    the row reuses the headline's eager timing instead."""
+    import torch
+
+    import paged_kv_decode_xs_amd as xs
+    import workloads as wl
+
+    w = wl.WORKLOADS[name]
+    row = {"workload": name, "description": w.description, "dtype": w.dtype, "partition_size": P,
+           "window": w.window, "sinks": w.sinks}
+    stream = torch.cuda.current_stream()
+    if headline is not None:
+        case, R = headline["case"], headline["R"]
+        step_ms, eager_ms, timing = headline["ms_step"], headline["ms_step"], "eager back-to-back steps"
+    else:
+        case, steps = rotated_steps(w, P, fused)
+        R = len(steps)
+        for i in range(min(warmup, R)):
+            steps[i].run(stream)
+        torch.cuda.synchronize()
+        eager_ms = time_calls(lambda i: steps[i % R].run(stream), min(K, 4 * R), stream)
+        graph = xs.StepGraph(steps)
+        graph.launch(stream)
+        torch.cuda.synchronize()
+        reps = max(1, math.ceil(min_steps / R))
+        reps = max(1, min(reps, math.ceil(200.0 / max(eager_ms * R, 1e-3))))
+        step_ms = time_calls(lambda i: graph.launch(stream), reps, stream) / R
+        graph.close()
+        del steps, graph
+        torch.cuda.empty_cache()
+        timing = f"HIP graph of {R} steps (one per pool copy), replayed {reps}x"
+    ab = algorithmic_bytes(case, P)
+    kernels = (["paged_attn_decode_append (fused append + decode)"] if fused else
+               ["kv_append", "paged_attn_decode"]) + (["paged_attn_reduce"] if P > 0 else [])
+    achieved = ab["step"] / (step_ms * 1e-3) / 1e9
+    traffic = read_traffic(name, P)
+    trace = read_trace(name, P)
+    row.update({
+        "pool_copies_rotated": R,
+        "kv_bytes_per_step": ab["kv"],
+        "step_kernels": kernels,
+        "step_us": round(step_ms * 1e3, 2),
+        "step_timing": timing,
+        "eager_step_us": round(eager_ms * 1e3, 2),
+        "kv_GBps": round(ab["kv"] / (step_ms * 1e-3) / 1e9, 2),
+        "seqs_per_s": round(w.batch / (step_ms * 1e-3), 1),
+        "pct_of_hbm_peak": round(100 * ab["kv"] / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None if traffic is None else
+            round((traffic["decode"] + traffic["reduce"]) / (step_ms * 1e-3) / 1e9, 2),
+            "algorithmic_bytes_per_step": ab["step"],
+        },
+        "trace_step_kernels_us": None if trace is None else round(trace["decode_us"] + trace["reduce_us"], 2),
+    })
+    return row
 
 
 def self_checks(P: int) -> dict:
@@ -554,45 +656,21 @@ def prefill_row(name: str = "qwen3_8b_prefill_c512", reps: int = 20, partitions=
     }
 
 
-def extra_row(w, P: int, fused: bool, r) -> dict:
-    """One line of "extra_workloads": the same quantities as the headline, for another workload."""
-    case = r["case"]
-    ab = algorithmic_bytes(case, P)
-    decode_bytes = ab["decode"] + (ab["append"] if fused else 0)
-    # A fused unsplit step is one launch: back-to-back steps time it without the few microseconds
-    # an event pair adds, which matter at this size.
-    one_launch = fused and P == 0
-    decode_ms = r["ms_step"] if one_launch else r["decode_ms_mean"]
-    achieved = decode_bytes / (decode_ms * 1e-3) / 1e9
-    return {
-        "workload": w.name,
-        "description": w.description,
-        "partition_size": P,
-        "window": w.window,
-        "sinks": w.sinks,
-        "pool_copies_rotated": r["R"],
-        "kv_bytes_per_step": ab["kv"],
-        "ms_per_step": round(r["ms_step"], 5),
-        "kv_GBps": round(ab["kv"] / (r["ms_step"] * 1e-3) / 1e9, 2),
-        "seqs_per_s": round(w.batch / (r["ms_step"] * 1e-3), 1),
-        "decode_launch_us": round(decode_ms * 1e3, 2),
-        "decode_timing": "back-to-back steps (one launch per step)" if one_launch else "HIP events around each launch",
-        "decode_algorithmic_GBps": round(achieved, 2),
-        "decode_frac_of_hbm_peak": round(achieved / HBM_PEAK_GBS, 4),
-    }
-
-
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="qwen3_8b_b64")
+    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--partition", type=int, default=None, help="split-K partition size (0 = no split)")
     ap.add_argument("--copies", type=int, default=None, help="pool copies to rotate through")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the extra workloads")
+    ap.add_argument("--no-extra", action="store_true", help="skip the config rows and every other extra row")
+    ap.add_argument("--only", default=None,
+                    help="time just this decode workload's row (cache-defeated graph replay) and print it")
+    ap.add_argument("--row-steps", type=int, default=2000,
+                    help="graph-replayed steps per decode row (at least; fewer for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed work, copy a 1 GiB buffer 5 times with torch (a plain copy kernel of "
                          "known size, to calibrate rocprofv3's FETCH_SIZE/WRITE_SIZE)")
@@ -607,8 +685,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: every step runs on a single device "
-              "(run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: this build runs every step on a single device and has no "
+              "multi-GPU path (run with --gpus 1)", file=sys.stderr)
         return 2
 
     import torch
@@ -627,13 +705,21 @@ def main() -> int:
         print(json.dumps({k: prefill_row(n, reps=reps, partitions=parts) for k, n in PREFILL_ROWS.items()
                           if args.prefill_workload in (None, n)}), flush=True)
         return 0
+    fused = not args.no_fuse
+    if args.only:
+        P = dict(CONFIGS + EXTRA_WORKLOADS).get(args.only, wl.WORKLOADS[args.only].partition_size)
+        P = P if args.partition is None else args.partition
+        row = decode_row(args.only, P, args.steps, args.warmup, fused, min_steps=args.row_steps)
+        if args.copy_calibration:
+            _copy_calibration()
+        print(json.dumps({"only": row}), flush=True)
+        return 0
 
     w = wl.WORKLOADS[args.workload]
-    P = w.partition_size if args.partition is None else args.partition
-    fused = not args.no_fuse
+    P = dict(CONFIGS).get(w.name, w.partition_size) if args.partition is None else args.partition
     K = args.steps
-    r = run_workload(w, P, fused, K, args.warmup, args.copies)
-    case, R, ms_step, decode_ms_mean = r["case"], r["R"], r["ms_step"], r["decode_ms_mean"]
+    r = run_headline(w, P, fused, K, args.warmup, args.copies)
+    case, R, ms_step, ms_decode = r["case"], r["R"], r["ms_step"], r["ms_decode"]
     stream = torch.cuda.current_stream()
 
     # Reference read rate of the device: the library's streaming-read probe over 2 GiB.
@@ -643,31 +729,20 @@ def main() -> int:
     achievable = {}
     for nt in (False, True):
         xs.xs_stream_read_probe(probe_buf, sink, nontemporal=nt, stream=stream)
-        best = float("inf")
-        for _ in range(5):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            xs.xs_stream_read_probe(probe_buf, sink, nontemporal=nt, stream=stream)
-            b.record(stream)
-            torch.cuda.synchronize()
-            best = min(best, a.elapsed_time(b))
+        best = min(time_calls(lambda i: xs.xs_stream_read_probe(probe_buf, sink, nontemporal=nt, stream=stream), 1,
+                              stream) for _ in range(5))
         achievable["nontemporal" if nt else "plain"] = round(probe_buf.numel() / (best * 1e-3) / 1e9, 1)
     del probe_buf
 
     if args.copy_calibration:
-        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        _copy_calibration()
 
     ab = algorithmic_bytes(case, P)
     kv_gbs = ab["kv"] / (ms_step * 1e-3) / 1e9
     decode_bytes = ab["decode"] + (ab["append"] if fused else 0)
-    achieved = decode_bytes / (decode_ms_mean * 1e-3) / 1e9
-    traffic_bytes = read_traffic(w.name, P, fused)
-    traffic = None if traffic_bytes is None else round(traffic_bytes / (decode_ms_mean * 1e-3) / 1e9, 2)
+    achieved = decode_bytes / (ms_decode * 1e-3) / 1e9
+    traffic = read_traffic(w.name, P)
+    trace = read_trace(w.name, P)
     result = {
         "metric": METRIC,
         "value": round(kv_gbs, 2),
@@ -697,7 +772,7 @@ def main() -> int:
         },
         "seqs_per_s": round(w.batch / (ms_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100 * kv_gbs / HBM_PEAK_GBS, 2),
-        "warm_cache_kv_GBps": round(ab["kv"] / (r["ms_step_warm"] * 1e-3) / 1e9, 2),
+        "warm_cache_kv_GBps": round(ab["kv"] / (r["ms_warm"] * 1e-3) / 1e9, 2),
         "achievable_read_GBps": achievable,
         "pct_of_achievable_nontemporal_read": round(100 * kv_gbs / achievable["nontemporal"], 2),
         "roofline": {
@@ -706,12 +781,14 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
+            "traffic": None if traffic is None else round(traffic["decode"] / (ms_decode * 1e-3) / 1e9, 2),
             "kernel": "paged_decode_mfma_kernel" + (" (fused append)" if fused else ""),
             "algorithmic_bytes_per_launch": decode_bytes,
-            "traffic_bytes_per_launch": traffic_bytes,
-            "mean_launch_us": round(decode_ms_mean * 1e3, 2),
-            "launch_us_p10_p50_p90": r["launch_us_p10_p50_p90"],
+            "traffic_bytes_per_launch": None if traffic is None else traffic["decode"],
+            "mean_launch_us": round(ms_decode * 1e3, 2),
+            "launch_timing": f"one HIP event pair around {K} back-to-back decode launches on rotated pools",
+            "group_mean_launch_us": r["decode_group_us"],
+            "trace_mean_launch_us": None if trace is None else trace["decode_us"],
         },
         "self_checks": self_checks(P),
     }
@@ -723,14 +800,13 @@ def main() -> int:
             log(f"[bench] PARITY FAILURE: {parity}")
     if not args.no_extra:
         rows = []
-        for name in EXTRA_WORKLOADS:
-            if name == w.name:
-                continue
-            we = wl.WORKLOADS[name]
+        for name, Pc in CONFIGS:
             torch.cuda.empty_cache()
-            rows.append(extra_row(we, we.partition_size, fused,
-                                  run_workload(we, we.partition_size, fused, min(K, 100), args.warmup)))
-        result["extra_workloads"] = rows
+            rows.append(decode_row(name, Pc, min(K, 200), args.warmup, fused,
+                                   headline=r if (name == w.name and Pc == P) else None, min_steps=args.row_steps))
+        result["configs"] = rows
+        result["extra_workloads"] = [decode_row(name, Pe, min(K, 200), args.warmup, fused, min_steps=args.row_steps)
+                                     for name, Pe in EXTRA_WORKLOADS]
         result["kv_swap"] = swap_row()
         for key, name in PREFILL_ROWS.items():
             result[key] = prefill_row(name)
@@ -742,6 +818,17 @@ def main() -> int:
     if not checks_ok:
         log(f"[bench] SELF-CHECK FAILURE: {result['self_checks']}")
     return 0 if result.get("parity_vs_oracle", {}).get("out_of_tolerance", 0) == 0 and checks_ok else 3
+
+
+def _copy_calibration() -> None:
+    import torch
+
+    src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 if __name__ == "__main__":

@@ -365,6 +365,7 @@ DecodeParams make_params(const DecodeArgs& a, int heads_per_wave) {
   p.num_blocks = a.num_blocks;
   p.part_blocks = a.partition_size > 0 ? a.partition_size / a.block_size : 0;
   p.max_partitions = a.max_partitions;
+  p.dense = 0;
   return p;
 }
 

@@ -51,6 +51,7 @@ struct DecodeParams {
   int window;             // 0: all positions
   int batch;
   int ncu;                // compute units of the device (the split grid's work order)
+  int dense;              // split grid: 1 = ranked item order (reads every length), 0 = partition-major ids
 };
 
 DecodeParams make_params(const DecodeArgs& a, int heads_per_wave);

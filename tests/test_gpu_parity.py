@@ -60,8 +60,8 @@ SHAPES = [
     ("bf16", 16, 16, 128, 16, [50, 51], 16),
     ("bf16", 24, 8, 128, 16, [77, 130], 32),   # group 3: one head per wavefront, 3 chunks
     ("bf16", 12, 2, 64, 16, [90, 260], 64),    # group 6: two heads per wavefront
-    ("bf16", 16, 2, 128, 16, [300, 45], 64),   # group 8
-    ("bf16", 32, 2, 128, 16, [129, 2], 48),    # group 16: two chunks of 8
+    ("bf16", 16, 2, 128, 16, [300, 45, 0], 64),   # group 8 (an empty row of 8 heads: zeros past 64 lanes)
+    ("bf16", 32, 2, 128, 16, [129, 2, 0], 48),    # group 16: two chunks of 8
     ("f32", 32, 2, 64, 16, [70, 18], 32),
 ]
 
@@ -175,15 +175,19 @@ def test_split_order_for_large_and_small_batches():
     # partition-major ids above that. Every order must give the oracle's result, with partitions
     # past a sequence's end, empty sequences, tied partial sizes and a last round that is not
     # whole mixed in.
+    # Partition size 64 on small grids takes partition-major ids; 256 the ranked order (2 to 256
+    # sequences).
     rng = np.random.default_rng(31)
-    for B in (64, 65, 256, 300):
-        lens = rng.integers(0, 400, B).tolist()
-        lens[3] = 0
-        lens[5] = 1
+    for B in (2, 64, 65, 256, 300):
+        lens = rng.integers(0, 1400, B).tolist()
+        lens[1] = 0
+        if B > 5:
+            lens[5] = 1
         case = _shape_case("bf16", 8, 2, 64, 16, lens, seed=32 + B)
-        ref = OracleResult(case, 64)
-        check_case(case, 64, ref, check_pools=False, label=f"split order B={B}")
-        check_case(case, 64, ref, label=f"split order B={B} fused", fused=True)
+        for P in (64, 256):
+            ref = OracleResult(case, P)
+            check_case(case, P, ref, check_pools=False, label=f"split order B={B} P={P}")
+            check_case(case, P, ref, label=f"split order B={B} P={P} fused", fused=True)
 
 
 @pytest.mark.parametrize("fused", [False, True])
@@ -214,3 +218,26 @@ def test_bad_block_ids_are_skipped(P, fused):
     got = as_f64(step.out)
     assert np.isfinite(got).all()
     assert_close(got, exp, *TOL["bf16"], f"bad block ids P={P} fused={fused}")
+
+
+def test_partition_overflow_gives_nan_rows():
+    # Sequence 1 needs 4 partitions of 64 tokens but the partials hold 2: the reduce writes its
+    # rows as NaN (a truncated context must not pass for a result); the others are unaffected.
+    import paged_kv_decode_xs_amd as xs
+    from tests.gpu_common import nan_fill
+
+    case = _shape_case("bf16", 8, 2, 128, 16, [100, 250, 0, 128], seed=81)
+    w = case.workload
+    ref = OracleResult(case)
+    dev = case_to_device(case)
+    step = xs.DecodeStep(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["context_lens"],
+                         dev["k_new"], dev["v_new"], w.scale, partition_size=64, max_context_len=128, fused=True)
+    assert step.part_m.shape[-1] == 2
+    nan_fill(step)
+    step.run()
+    torch.cuda.synchronize()
+    got = as_f64(step.out)
+    assert np.isnan(got[1]).all(), "the truncated sequence must give NaN rows"
+    keep = [0, 2, 3]
+    assert_close(got[keep], ref.out[keep], *TOL["bf16"], "partition overflow: the other sequences")
+    log("[gpu] partition overflow: NaN rows")
