@@ -134,6 +134,33 @@ int xs_paged_attn_decode_append(const void* q, const void* k_new, const void* v_
                                 int block_size, int max_blocks_per_seq, int num_blocks,
                                 int partition_size, int max_partitions, int dtype, void* stream);
 
+/* Bytes of the device-resident scratch behind xs_paged_attn_decode_append_noalloc (per device). */
+#define XS_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * xs_paged_attn_decode_append followed by xs_paged_attn_reduce, for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the split-K partials live in a scratch array inside the library
+ * (XS_NOALLOC_SCRATCH_BYTES per device, held from the first call on that device until the process
+ * ends) instead of in part_o/part_m/part_l. Nothing is allocated, by this call or the library.
+ * Arguments, results and the append are those of xs_paged_attn_decode_append and
+ * xs_paged_attn_reduce with the same partition_size and max_partitions; `out` [batch,
+ * num_q_heads, head_dim] (16-byte aligned) is always written, k_new and v_new are required.
+ * partition_size == 0 is the unsplit call (no scratch used). With split-K the partials take
+ * batch * num_q_heads * max_partitions * (head_dim + 2) * 4 bytes (each array rounded up to 256);
+ * more than XS_NOALLOC_SCRATCH_BYTES is XS_EINVAL, before any device work.
+ * Every call on a device shares that device's scratch and leaves its contents behind: two calls
+ * that may run at the same time on one device (other streams, other threads) race and give wrong
+ * results; calls on one stream are ordered and safe.
+ */
+int xs_paged_attn_decode_append_noalloc(const void* q, const void* k_new, const void* v_new,
+                                        void* k_cache, void* v_cache,
+                                        const int32_t* block_tables, const int32_t* context_lens,
+                                        float scale, void* out,
+                                        int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                        int block_size, int max_blocks_per_seq, int num_blocks,
+                                        int partition_size, int max_partitions, int dtype, void* stream);
+
 /*
  * Decode attention (and, if k_new/v_new are given, the append) with an even split of the work:
  * writes `out` directly, with no partition size to choose. The result is the decode attention

@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     xs_paged_attn_decode,
     xs_paged_attn_balanced_workspace_size,
     xs_paged_attn_decode_append,
+    xs_paged_attn_decode_append_noalloc,
     xs_paged_attn_decode_balanced,
     xs_paged_attn_decode_sinks,
     xs_paged_attn_prefill,

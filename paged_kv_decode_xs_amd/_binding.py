@@ -56,6 +56,8 @@ SIGNATURES = {
     "xs_paged_attn_decode_append": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _vp,
                                     _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp],
     "xs_paged_attn_reduce": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp],
+    "xs_paged_attn_decode_append_noalloc": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _vp,
+                                            _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp],
     "xs_paged_attn_decode_balanced": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, ctypes.c_size_t,
                                       _i, _i, _i, _i, _i, _i, _i, _i, _vp],
     "xs_paged_attn_balanced_workspace_size": [_i, _i, _i, _i],
@@ -226,6 +228,30 @@ def xs_paged_attn_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: tor
         _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         float(scale), _ptr(out), _ptr(part_o), _ptr(part_m), _ptr(part_l), B, Hq, Hkv, D, BS,
         block_tables.shape[1], NB, int(partition_size), NP, _dtype_code(q), _stream_handle(stream)))
+
+
+def xs_paged_attn_decode_append_noalloc(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                                        k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                                        context_lens: torch.Tensor, scale: float, out: torch.Tensor,
+                                        partition_size: int = 0, max_partitions: Optional[int] = None,
+                                        stream=None) -> None:
+    """Append + decode (+ the reduce with split-K) into `out`, the partials kept in the library's
+    own device scratch: nothing is allocated. max_partitions defaults to what the block table can
+    hold (max_blocks_per_seq * block_size / partition_size)."""
+    B, Hq, Hkv, D, BS, NB, _ = _decode_common(q, k_cache, v_cache, block_tables, context_lens, out, None, None,
+                                              None, 0)
+    _dev(k_new, v_new)
+    _need(k_new.shape == (B, Hkv, D) and v_new.shape == (B, Hkv, D), "k_new/v_new must be [batch, Hkv, D]")
+    _need(k_new.dtype == q.dtype and v_new.dtype == q.dtype, "k_new/v_new dtype differs from q")
+    NP = 0
+    if partition_size > 0:
+        NP = max_partitions if max_partitions is not None else num_partitions(block_tables.shape[1] * BS,
+                                                                              partition_size)
+    lib = load_library()
+    _check("xs_paged_attn_decode_append_noalloc", lib.xs_paged_attn_decode_append_noalloc(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        float(scale), _ptr(out), B, Hq, Hkv, D, BS, block_tables.shape[1], NB, int(partition_size), int(NP),
+        _dtype_code(q), _stream_handle(stream)))
 
 
 def xs_paged_attn_reduce(part_o: torch.Tensor, part_m: torch.Tensor, part_l: torch.Tensor,

@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -192,6 +193,91 @@ XS_API int xs_paged_attn_decode_append(const void* q, const void* k_new, const v
   if (!aligned16(k_new) || !aligned16(v_new)) return fail(XS_EINVAL, "%s: k_new and v_new must be 16-byte aligned", who);
   (void)hipGetLastError();
   return launch_status(who, xs::launch_paged_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------------------------------------
+// The decode step without a workspace argument: the split-K partials live in a file-scope
+// device array. Each device holds its own copy of the array, at its own address; host code never
+// passes the array's name to a kernel (on the host it is only a stand-in), only the device address
+// that hipGetSymbolAddress gives for the current device, looked up once per device.
+
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[XS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on the first call on that device).
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+XS_API int xs_paged_attn_decode_append_noalloc(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                               void* v_cache, const int32_t* block_tables,
+                                               const int32_t* context_lens, float scale, void* out, int batch,
+                                               int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                               int max_blocks_per_seq, int num_blocks, int partition_size,
+                                               int max_partitions, int dtype, void* stream) {
+  const char* who = "xs_paged_attn_decode_append_noalloc";
+  // Checked as the split call with partials (stand-in pointers: the real ones come below).
+  float* const stand_in = reinterpret_cast<float*>(static_cast<uintptr_t>(256));
+  const bool split = partition_size > 0;
+  xs::DecodeArgs a = decode_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
+                                 split ? nullptr : out, split ? stand_in : nullptr, split ? stand_in : nullptr,
+                                 split ? stand_in : nullptr, batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                                 max_blocks_per_seq, num_blocks, partition_size, max_partitions, dtype);
+  const int st = check_decode(who, a, dtype);
+  if (st != XS_OK) return st;
+  if (batch == 0) return ok();
+  if (!out || !aligned16(out)) return fail(XS_EINVAL, "%s: out must be a 16-byte aligned pointer", who);
+  if (!k_new || !v_new) return fail(XS_EINVAL, "%s: k_new and v_new must not be NULL", who);
+  if (!aligned16(k_new) || !aligned16(v_new)) return fail(XS_EINVAL, "%s: k_new and v_new must be 16-byte aligned", who);
+  a.out = out;
+  size_t o_bytes = 0, ml_bytes = 0;
+  if (split) {
+    const size_t rows = (size_t)batch * num_q_heads * (size_t)max_partitions;
+    o_bytes = align256(rows * head_dim * sizeof(float));
+    ml_bytes = align256(rows * sizeof(float));
+    const size_t need = o_bytes + 2 * ml_bytes;
+    if (need > (size_t)XS_NOALLOC_SCRATCH_BYTES)
+      return fail(XS_EINVAL,
+                  "%s: the partials need %zu bytes (batch * num_q_heads * max_partitions * (head_dim + 2) * 4, "
+                  "rounded); the scratch holds %zu: use xs_paged_attn_decode_append with caller buffers",
+                  who, need, (size_t)XS_NOALLOC_SCRATCH_BYTES);
+  }
+  (void)hipGetLastError();
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!split) return launch_status(who, xs::launch_paged_decode(a, s));
+  void* base = nullptr;
+  const hipError_t e = scratch_address(&base);
+  if (e != hipSuccess) return fail(XS_ELAUNCH, "%s: hipGetSymbolAddress: %s", who, hipGetErrorString(e));
+  unsigned char* p = static_cast<unsigned char*>(base);
+  a.part_o = reinterpret_cast<float*>(p);
+  a.part_m = reinterpret_cast<float*>(p + o_bytes);
+  a.part_l = reinterpret_cast<float*>(p + o_bytes + ml_bytes);
+  hipError_t le = xs::launch_paged_decode(a, s);
+  if (le == hipSuccess)
+    le = xs::launch_paged_reduce(a.part_o, a.part_m, a.part_l, context_lens, out, batch, num_q_heads, head_dim,
+                                 partition_size, a.max_partitions, a.bf16, s);
+  return launch_status(who, le);
 }
 
 XS_API int xs_paged_attn_decode_sinks(const void* q, const void* k_new, const void* v_new, void* k_cache,

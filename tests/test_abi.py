@@ -406,3 +406,28 @@ def test_prefill_sinks_rejects(kw, status, needle):
 def test_prefill_sinks_empty_is_a_noop():
     assert _prefill_sinks(batch=0, q=None, out=None) == 0
     assert _prefill_sinks(c=0, q=None, out=None, p=64, np_=1) == 0
+
+
+def test_noalloc_rejects_partials_beyond_its_scratch():
+    # 64 sequences x 32 heads x 1024 partitions x 130 floats is far beyond the scratch: XS_EINVAL,
+    # decided on the host before any device work.
+    lib = xb.load_library()
+    st = lib.xs_paged_attn_decode_append_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.125, FAKE, 64, 32, 8,
+                                                 128, 16, 4096, 8192, 64, 1024, B, None)
+    assert st == 1
+    assert "scratch holds" in xb.xs_last_error()
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(out=None), "out must be"),
+    (dict(k_new=None), "k_new and v_new"),
+    (dict(p=24), "multiple of block_size"),
+])
+def test_noalloc_host_checks(kw, needle):
+    a = dict(q=FAKE, k_new=FAKE, v_new=FAKE, out=FAKE, p=32)
+    a.update(kw)
+    lib = xb.load_library()
+    st = lib.xs_paged_attn_decode_append_noalloc(a["q"], a["k_new"], FAKE, FAKE, FAKE, FAKE, FAKE, 0.125, a["out"],
+                                                 2, 8, 2, 128, 16, 4, 16, a["p"], 2, B, None)
+    assert st == 1
+    assert needle in xb.xs_last_error()
