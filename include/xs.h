@@ -162,31 +162,6 @@ int xs_paged_attn_decode_append_noalloc(const void* q, const void* k_new, const 
                                         int partition_size, int max_partitions, int dtype, void* stream);
 
 /*
- * Decode attention (and, if k_new/v_new are given, the append) with an even split of the work:
- * writes `out` directly, with no partition size to choose. The result is the decode attention
- * above (and the same append as xs_kv_append); only the rounding order differs from the
- * split-K calls.
- * The batch's 16-token tiles (sequence b has ceil(L_b / 16) per kv head) are cut into equal
- * contiguous ranges, one per wavefront of the device, and each range is streamed without
- * pause. Where a (sequence, kv head) is cut, its parts leave partials in `workspace` that a
- * second kernel of the same call merges with the log-sum-exp rule of xs_paged_attn_reduce.
- * `workspace` (device, 16-byte aligned, caller-owned, contents not preserved) must hold
- * xs_paged_attn_balanced_workspace_size(batch, num_q_heads, num_kv_heads, head_dim) bytes for
- * the current device. Supported: bf16, head_dim 64 or 128, block_size 16 or 32.
- * Sources: as xs_paged_attn_decode and xs_kv_append; the split is this library's.
- */
-int xs_paged_attn_decode_balanced(const void* q, const void* k_new, const void* v_new,
-                                  void* k_cache, void* v_cache,
-                                  const int32_t* block_tables, const int32_t* context_lens,
-                                  float scale, void* out, void* workspace, size_t workspace_bytes,
-                                  int batch, int num_q_heads, int num_kv_heads, int head_dim,
-                                  int block_size, int max_blocks_per_seq, int num_blocks,
-                                  int dtype, void* stream);
-
-/* Workspace bytes xs_paged_attn_decode_balanced needs on the current device (0 for bad sizes). */
-size_t xs_paged_attn_balanced_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim);
-
-/*
  * Decode attention with attention sinks and a sliding window (xserv compare
  * phase10...cf1e9e41, attention.rs, `paged_decode_attention_sinks` and its FFI
  * `launch_paged_decode_attention_sinks_bf16`), optionally with the fused append.

@@ -17,10 +17,8 @@ from ._binding import (  # noqa: F401
     xs_kv_swap_out,
     xs_last_error,
     xs_paged_attn_decode,
-    xs_paged_attn_balanced_workspace_size,
     xs_paged_attn_decode_append,
     xs_paged_attn_decode_append_noalloc,
-    xs_paged_attn_decode_balanced,
     xs_paged_attn_decode_sinks,
     xs_paged_attn_prefill,
     xs_paged_attn_prefill_sinks,

@@ -58,9 +58,6 @@ SIGNATURES = {
     "xs_paged_attn_reduce": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp],
     "xs_paged_attn_decode_append_noalloc": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _vp,
                                             _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp],
-    "xs_paged_attn_decode_balanced": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, ctypes.c_size_t,
-                                      _i, _i, _i, _i, _i, _i, _i, _i, _vp],
-    "xs_paged_attn_balanced_workspace_size": [_i, _i, _i, _i],
     "xs_paged_attn_decode_sinks": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _f, _vp, _vp, _vp, _vp,
                                    _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp],
     "xs_paged_attn_reduce_sinks": [_vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _vp],
@@ -105,8 +102,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         for name, args in SIGNATURES.items():
             fn = getattr(lib, name)
             fn.argtypes = args
-            fn.restype = {"xs_last_error": ctypes.c_char_p,
-                          "xs_paged_attn_balanced_workspace_size": ctypes.c_size_t}.get(name, ctypes.c_int)
+            fn.restype = ctypes.c_char_p if name == "xs_last_error" else ctypes.c_int
         if path is None:
             _lib = lib
         return lib
@@ -266,30 +262,6 @@ def xs_paged_attn_reduce(part_o: torch.Tensor, part_m: torch.Tensor, part_l: tor
     _check("xs_paged_attn_reduce", lib.xs_paged_attn_reduce(
         _ptr(part_o), _ptr(part_m), _ptr(part_l), _ptr(context_lens), _ptr(out), B, Hq, D,
         int(partition_size), NP, _dtype_code(out), _stream_handle(stream)))
-
-
-def xs_paged_attn_balanced_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int) -> int:
-    """Bytes of workspace xs_paged_attn_decode_balanced needs on the current device."""
-    return int(load_library().xs_paged_attn_balanced_workspace_size(batch, num_q_heads, num_kv_heads, head_dim))
-
-
-def xs_paged_attn_decode_balanced(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                                  block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
-                                  out: torch.Tensor, workspace: torch.Tensor, k_new: Optional[torch.Tensor] = None,
-                                  v_new: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Decode attention (plus the append when k_new/v_new are given) with an even split of the work."""
-    B, Hq, Hkv, D, BS, NB, _ = _decode_common(q, k_cache, v_cache, block_tables, context_lens, out, None, None,
-                                              None, 0)
-    _dev(k_new, v_new, workspace)
-    if k_new is not None or v_new is not None:
-        _need(k_new is not None and v_new is not None, "give both k_new and v_new, or neither")
-        _need(k_new.shape == (B, Hkv, D) and v_new.shape == (B, Hkv, D), "k_new/v_new must be [batch, Hkv, D]")
-        _need(k_new.dtype == q.dtype and v_new.dtype == q.dtype, "k_new/v_new dtype differs from q")
-    lib = load_library()
-    _check("xs_paged_attn_decode_balanced", lib.xs_paged_attn_decode_balanced(
-        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
-        float(scale), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), B, Hq, Hkv, D, BS,
-        block_tables.shape[1], NB, _dtype_code(q), _stream_handle(stream)))
 
 
 def xs_paged_attn_decode_sinks(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -355,38 +355,6 @@ XS_API int xs_paged_attn_reduce(const float* part_o, const float* part_m, const 
                                                     static_cast<hipStream_t>(stream)));
 }
 
-XS_API size_t xs_paged_attn_balanced_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim) {
-  if (batch < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 || head_dim < 1) return 0;
-  return xs::balanced_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, xs::balanced_workers());
-}
-
-XS_API int xs_paged_attn_decode_balanced(const void* q, const void* k_new, const void* v_new, void* k_cache,
-                                         void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
-                                         float scale, void* out, void* workspace, size_t workspace_bytes, int batch,
-                                         int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                                         int max_blocks_per_seq, int num_blocks, int dtype, void* stream) {
-  const char* who = "xs_paged_attn_decode_balanced";
-  const xs::DecodeArgs a = decode_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out,
-                                       nullptr, nullptr, nullptr, batch, num_q_heads, num_kv_heads, head_dim,
-                                       block_size, max_blocks_per_seq, num_blocks, 0, 0, dtype);
-  const int st = check_decode(who, a, dtype);
-  if (st != XS_OK) return st;
-  if (!xs::balanced_supported(dtype == XS_BF16, head_dim, block_size))
-    return fail(XS_EUNSUPPORTED, "%s: needs bf16, head_dim 64 or 128 and block_size 16 or 32", who);
-  if (batch == 0) return ok();
-  if ((k_new == nullptr) != (v_new == nullptr))
-    return fail(XS_EINVAL, "%s: k_new and v_new must both be given or both be NULL", who);
-  if (k_new && (!aligned16(k_new) || !aligned16(v_new)))
-    return fail(XS_EINVAL, "%s: k_new and v_new must be 16-byte aligned", who);
-  const int workers = xs::balanced_workers();
-  const size_t need = xs::balanced_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, workers);
-  if (!workspace || workspace_bytes < need)
-    return fail(XS_EINVAL, "%s: workspace of %zu bytes needed, %zu given", who, need, workspace ? workspace_bytes : 0);
-  if (!aligned16(workspace)) return fail(XS_EINVAL, "%s: workspace must be 16-byte aligned", who);
-  (void)hipGetLastError();
-  return launch_status(who, xs::launch_paged_decode_balanced(a, workspace, workers, static_cast<hipStream_t>(stream)));
-}
-
 XS_API int xs_stream_read_probe(const void* buf, size_t bytes, unsigned* sink, int nontemporal, void* stream) {
   const char* who = "xs_stream_read_probe";
   if (!buf || !sink) return fail(XS_EINVAL, "%s: buf and sink must not be NULL", who);

@@ -56,25 +56,6 @@ struct DecodeParams {
 
 DecodeParams make_params(const DecodeArgs& a, int heads_per_wave);
 
-// Balanced decode (see xs_decode_balanced.hip): `workers` wavefronts split the batch's tiles
-// evenly; piece partials go to `ws_*`, sized for batch*num_q_heads + workers*GC rows.
-struct BalancedParams {
-  DecodeParams d;
-  float* ws_o;  // [rows, head_dim]
-  float* ws_m;  // [rows]
-  float* ws_l;  // [rows]
-  int batch;
-  int block_size;
-  int workers;
-  int min_tiles;  // fewest tiles per worker
-};
-
-// Workers of the balanced decode on the current device, and the workspace it needs.
-int balanced_workers();
-size_t balanced_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim, int workers);
-bool balanced_supported(bool bf16, int head_dim, int block_size);
-hipError_t launch_paged_decode_balanced(const DecodeArgs& a, void* workspace, int workers, hipStream_t stream);
-
 hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                             const int32_t* block_tables, const int32_t* context_lens, int batch,
                             int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,

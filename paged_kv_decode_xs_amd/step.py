@@ -4,10 +4,8 @@
 chains the library calls on one stream. With partition_size == 0 it issues the unsplit decode
 and no reduce. With fused=True the append and the decode are one call
 (xs_paged_attn_decode_append); otherwise they are xs_kv_append then xs_paged_attn_decode.
-With schedule="balanced" the step is xs_paged_attn_decode_balanced (append included when fused;
-otherwise xs_kv_append first), which writes `out` itself; partition_size is then unused.
 With sinks (bf16 [Hq]) or window > 0 the decode and the reduce are xs_paged_attn_decode_sinks and
-xs_paged_attn_reduce_sinks (split schedule only).
+xs_paged_attn_reduce_sinks.
 `DecodeStep.capture()` records the same step as one HIP graph (xs_step_graph_create); replaying it
 runs the step on the buffers as they are at replay time.
 `suggest_partition_size` picks a split partition size from a batch's context lengths (host side).
@@ -52,20 +50,15 @@ class DecodeStep:
     def __init__(self, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
                  context_lens: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, scale: float,
                  partition_size: int = 0, max_context_len: Optional[int] = None, fused: bool = False,
-                 schedule: str = "split", sinks: Optional[torch.Tensor] = None, window: int = 0):
+                 sinks: Optional[torch.Tensor] = None, window: int = 0):
         self.q, self.k_cache, self.v_cache = q, k_cache, v_cache
         self.block_tables, self.context_lens = block_tables, context_lens
         self.k_new, self.v_new = k_new, v_new
         self.scale = float(scale)
         self.partition_size = int(partition_size)
         self.fused = bool(fused)
-        if schedule not in ("split", "balanced"):
-            raise ValueError(f"unknown schedule {schedule!r}")
-        self.schedule = schedule
         self.sinks, self.window = sinks, int(window)
         self.sw = sinks is not None or self.window > 0
-        if self.sw and schedule != "split":
-            raise ValueError("sinks and windows run on the split schedule")
         B, Hq, D = q.shape
         self.out = torch.empty((B, Hq, D), dtype=q.dtype, device=q.device)
         if self.partition_size > 0:
@@ -78,12 +71,6 @@ class DecodeStep:
             self.part_l = torch.empty((B, Hq, NP), dtype=torch.float32, device=q.device)
         else:
             self.part_o = self.part_m = self.part_l = None
-        self.workspace = None
-        if schedule == "balanced":
-            self.partition_size = 0
-            self.part_o = self.part_m = self.part_l = None
-            nbytes = xb.xs_paged_attn_balanced_workspace_size(B, Hq, k_cache.shape[1], D)
-            self.workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
 
     def append(self, stream=None) -> None:
         xb.xs_kv_append(self.k_new, self.v_new, self.k_cache, self.v_cache, self.block_tables, self.context_lens,
@@ -124,22 +111,11 @@ class DecodeStep:
                                        part_o=self.part_o, part_m=self.part_m, part_l=self.part_l,
                                        partition_size=self.partition_size, stream=stream)
 
-    def balanced(self, stream=None) -> None:
-        xb.xs_paged_attn_decode_balanced(self.q, self.k_cache, self.v_cache, self.block_tables, self.context_lens,
-                                         self.scale, self.out, self.workspace,
-                                         k_new=self.k_new if self.fused else None,
-                                         v_new=self.v_new if self.fused else None, stream=stream)
-
     def capture(self) -> "StepGraph":
-        """This step (split schedule) as one HIP graph."""
+        """This step as one HIP graph."""
         return StepGraph([self])
 
     def run(self, stream=None) -> torch.Tensor:
-        if self.schedule == "balanced":
-            if not self.fused:
-                self.append(stream)
-            self.balanced(stream)
-            return self.out
         if self.fused:
             self.append_and_attend(stream)
         else:
@@ -174,9 +150,6 @@ class StepGraph:
 
     def __init__(self, steps):
         self._steps = list(steps)  # keeps the captured buffers alive
-        for s in self._steps:
-            if s.schedule != "split":
-                raise ValueError("graph capture covers the split schedule")
         self._handle = xb.xs_step_graph_create([_step_desc(s) for s in self._steps])
 
     def launch(self, stream=None) -> torch.Tensor:

@@ -59,10 +59,10 @@ class OracleResult:
 
 
 def run_step(dev: Dict[str, torch.Tensor], scale: float, partition_size: int, max_context_len: int = None,
-             fused: bool = False, schedule: str = "split"):
+             fused: bool = False):
     step = xs.DecodeStep(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["context_lens"],
                          dev["k_new"], dev["v_new"], scale, partition_size=partition_size,
-                         max_context_len=max_context_len, fused=fused, schedule=schedule)
+                         max_context_len=max_context_len, fused=fused)
     nan_fill(step)
     step.run()
     torch.cuda.synchronize()
@@ -78,23 +78,23 @@ def nan_fill(step) -> None:
 
 
 def check_case(case, partition_size: int, ref: OracleResult = None, check_pools: bool = True, label: str = "",
-               fused: bool = False, schedule: str = "split"):
+               fused: bool = False):
     """Append + decode (+ reduce) on the GPU, compared with the oracle. Returns the max output error."""
     w = case.workload
     log(f"[gpu] {label or w.name}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim} "
-        f"BS={w.block_size} dtype={w.dtype} P={partition_size} fused={fused} schedule={schedule} "
+        f"BS={w.block_size} dtype={w.dtype} P={partition_size} fused={fused} "
         f"lens={case.context_lens[:8].tolist()}...")
     ref = ref or OracleResult(case, partition_size)
     dev = case_to_device(case)
     step = run_step(dev, w.scale, partition_size, int(case.context_lens.max(initial=1)) if partition_size else None,
-                    fused=fused, schedule=schedule)
+                    fused=fused)
     if check_pools:
         for name, exp in (("k_cache", ref.k_pool), ("v_cache", ref.v_pool)):
             got = to_numpy_bits(dev[name])
             assert np.array_equal(got.view(np.uint8), exp.view(np.uint8)), f"{name} differs after append"
     atol, rtol = TOL[w.dtype]
     err = assert_close(as_f64(step.out), ref.out, atol, rtol, f"{label or w.name} out (P={partition_size})")
-    if schedule == "split" and partition_size > 0 and ref.stats is not None:
+    if partition_size > 0 and ref.stats is not None:
         check_partials(step, ref, case)
     return err, step, dev
 
