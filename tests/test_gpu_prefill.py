@@ -28,6 +28,7 @@ import torch
 import oracle
 import paged_kv_decode_xs_amd as xs
 from tests.gpu_common import TOL, as_f64, assert_close, log
+from tests.rounding_bound import assert_rounding_bound, prefill_spread
 from workloads.device import to_numpy_bits, to_torch
 from workloads.prefill import PREFILL_WORKLOADS, PrefillWorkload, make_prefill_case
 
@@ -56,10 +57,17 @@ def _to_dev(case):
 
 
 def _attend(dev, scale, split=None):
+    # Output and partials start as NaN: whatever the kernels leave unwritten shows in the result.
+    out = torch.full_like(dev["q"], float("nan"))
     if split:
+        B, Hq, C, D = dev["q"].shape
+        NP = xs.num_partitions(dev["bt"].shape[1] * dev["k_cache"].shape[2], split)
+        po = torch.full((B, Hq, C, NP, D), float("nan"), dtype=torch.float32, device="cuda")
+        pml = torch.full((B, Hq, C, NP, 2), float("nan"), dtype=torch.float32, device="cuda")
         return xs.xs_paged_attn_prefill_split(dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"], dev["sp"], dev["cl"],
-                                              scale, split)
-    return xs.xs_paged_attn_prefill(dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"], dev["sp"], dev["cl"], scale)
+                                              scale, split, out=out, part_o=po, part_ml=pml)
+    return xs.xs_paged_attn_prefill(dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"], dev["sp"], dev["cl"], scale,
+                                    out=out)
 
 
 def _run(dev, scale, split=None):
@@ -89,6 +97,9 @@ def _full_check(w, label, split=None):
     got = as_f64(out)
     atol, rtol = TOL["bf16"]
     err = assert_close(got, exp, atol, rtol, f"prefill {label} split={split}")
+    tau = prefill_spread(case.q, kp, vp, case.block_tables, case.start_pos, case.chunk_lens, w.scale, w.block_size,
+                         "bf16")
+    assert_rounding_bound(got, exp, tau, f"prefill {label} split={split}, rounding bound")
     for b, n in enumerate(case.chunk_lens.tolist()):
         assert not got[b, :, n:].any(), f"rows past chunk_lens[{b}] = {n} are not zero"
     # Deterministic: a second run on the same inputs gives the same bits.
@@ -260,6 +271,10 @@ def test_qwen3_prefill_workload_sampled_rows(name, split):
                                                  case.start_pos[b:b + 1] + a, np.array([k], np.int32), w.scale,
                                                  w.block_size, "bf16")
             assert_close(got[b:b + 1, :, a:a + k], exp[:, :, :k], atol, rtol, f"{w.name} b={b} rows {a}..{a + k - 1}")
+            tau = prefill_spread(case.q[b:b + 1], kp, vp, case.block_tables[b:b + 1], case.start_pos[b:b + 1],
+                                 case.chunk_lens[b:b + 1], w.scale, w.block_size, "bf16", b_rows={0: (a, a + k)})
+            assert_rounding_bound(got[b:b + 1, :, a:a + k], exp[:, :, :k], tau[:, :, a:a + k],
+                                  f"{w.name} b={b} rows {a}..{a + k - 1}, rounding bound")
 
 
 @pytest.mark.parametrize("decode_split", [0, 64])

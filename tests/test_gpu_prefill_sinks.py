@@ -20,6 +20,7 @@ import torch
 import oracle
 import paged_kv_decode_xs_amd as xs
 from tests.gpu_common import TOL, as_f64, assert_close, log
+from tests.rounding_bound import assert_rounding_bound, prefill_spread
 from tests.test_gpu_prefill import SHAPES, _shape_workload, _to_dev
 from workloads import f32_to_bf16_bits
 from workloads.device import to_torch
@@ -40,9 +41,18 @@ def _sinks_dev(case):
 
 
 def _attend(dev, case, window, split=0):
+    # Output and partials start as NaN: whatever the kernels leave unwritten shows in the result.
     w = case.workload
+    out = torch.full_like(dev["q"], float("nan"))
+    po = pml = None
+    if split:
+        B, Hq, C, D = dev["q"].shape
+        NP = xs.num_partitions(dev["bt"].shape[1] * dev["k_cache"].shape[2], split)
+        po = torch.full((B, Hq, C, NP, D), float("nan"), dtype=torch.float32, device="cuda")
+        pml = torch.full((B, Hq, C, NP, 2), float("nan"), dtype=torch.float32, device="cuda")
     return xs.xs_paged_attn_prefill_sinks(dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"], dev["sp"], dev["cl"],
-                                          w.scale, sinks=_sinks_dev(case), window_size=window, partition_size=split)
+                                          w.scale, sinks=_sinks_dev(case), window_size=window, partition_size=split,
+                                          out=out, part_o=po, part_ml=pml)
 
 
 def _append(dev):
@@ -63,11 +73,14 @@ def test_prefill_sinks_matches_oracle(shape, window, sinks):
     dev = _to_dev(case)
     _append(dev)
     atol, rtol = TOL["bf16"]
+    tau = prefill_spread(case.q, kp, vp, case.block_tables, case.start_pos, case.chunk_lens, w.scale, w.block_size,
+                         "bf16", sinks=case.sinks, window=window)
     for split in (0, 64):
         out = _attend(dev, case, window, split)
         torch.cuda.synchronize()
         got = as_f64(out)
         assert_close(got, exp, atol, rtol, f"prefill sinks window={window} sinks={sinks} split={split}")
+        assert_rounding_bound(got, exp, tau, f"prefill sinks window={window} sinks={sinks} split={split}, bound")
         for b, n in enumerate(case.chunk_lens.tolist()):
             assert not got[b, :, n:].any(), f"rows past chunk_lens[{b}] = {n} are not zero"
         again = _attend(dev, case, window, split)

@@ -14,7 +14,8 @@ import torch
 
 import oracle
 import workloads as wl
-from tests.gpu_common import P_BF16_REL, PART_TOL, TOL, as_f64, assert_close, log
+from tests.gpu_common import P_BF16_REL, PART_TOL, TOL, as_f64, assert_close, log, nan_fill
+from tests.rounding_bound import assert_rounding_bound, decode_spread
 from workloads.device import case_to_device, to_numpy_bits
 
 pytestmark = pytest.mark.gpu
@@ -51,12 +52,17 @@ def run_case(case, window, sink_bits, P, fused, check_parts=True, label=""):
     step = xs.DecodeStep(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["context_lens"],
                          dev["k_new"], dev["v_new"], w.scale, partition_size=P, max_context_len=maxlen if P else None,
                          fused=fused, sinks=_sinks_tensor(sink_bits), window=window)
+    nan_fill(step)
     step.run()
     torch.cuda.synchronize()
     for name, exp in (("k_cache", k_pool), ("v_cache", v_pool)):
         assert np.array_equal(to_numpy_bits(dev[name]).view(np.uint8), exp.view(np.uint8)), f"{name} after append"
     atol, rtol = TOL[w.dtype]
-    err = assert_close(as_f64(step.out), ref, atol, rtol, f"{label} out")
+    got = as_f64(step.out)
+    err = assert_close(got, ref, atol, rtol, f"{label} out")
+    tau = decode_spread(case.q, k_pool, v_pool, case.block_tables, case.context_lens, w.scale, w.block_size, "bf16",
+                        sinks=sink_bits, window=window)
+    assert_rounding_bound(got, ref, tau, f"{label} out, rounding bound")
     if P > 0 and check_parts:
         _, stats = oracle.split_paged_decode_attention_sinks(case.q, k_pool, v_pool, case.block_tables,
                                                              case.context_lens, w.scale, w.block_size, w.dtype, P,
