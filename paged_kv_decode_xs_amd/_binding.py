@@ -20,7 +20,9 @@ from typing import Optional
 import torch
 
 LIB_NAME = "libxs.so"
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+# XS_LIBRARY names another build of the same library (the host-sanitized one the ABI tests run
+# under); there is no fallback either way.
+LIB_PATH = os.environ.get("XS_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
 
 XS_F32 = 0
 XS_BF16 = 1
