@@ -1,5 +1,5 @@
 /*
- * xs.h - C ABI of libxs.so: paged-KV decode attention for AMD MI355X (gfx950).
+ * xs/xs.h - C ABI of libxs.so: paged-KV decode attention for AMD MI355X (gfx950).
  *
  * One decode step of an LLM serving engine over a paged KV cache:
  *   1. xs_kv_append          writes each running sequence's new K/V row into its block.
@@ -31,6 +31,9 @@
  *       context_lens    int32 [batch]; L_b = the context length of sequence b AFTER this
  *                       step's append, i.e. the index of the just-written token + 1.
  *   - dtype: q, k_new, v_new, the pools and out all have the same dtype (XS_F32 or XS_BF16).
+ *     Parameters named dtype are plain ints carrying an xs_dtype value: any other value is
+ *     rejected with XS_EUNSUPPORTED (an enum-typed parameter would make such a value undefined
+ *     behaviour in C++ instead of an error).
  *     Arithmetic is fp32. bf16 results are rounded to nearest-even.
  *   - Supported: head_dim in {64, 128}; block_size in {8, 16, 32}; num_q_heads a multiple
  *     of num_kv_heads; q, pools, k_new/v_new, out and part_o 16-byte aligned.

@@ -1,6 +1,6 @@
 """Paged-KV decode attention for AMD MI355X (gfx950).
 
-The computation lives in libxs.so (hand-written HIP kernels behind the C ABI in include/xs.h).
+The computation lives in libxs.so (hand-written HIP kernels behind the C ABI in include/xs/xs.h).
 This package is its thin Python binding plus a decode-step helper that chains the three calls.
 """
 

@@ -1,7 +1,7 @@
 """ctypes binding of libxs.so: argument marshalling only.
 
 Each function takes torch tensors, reads their shapes and device pointers, and calls the C
-function of the same name in libxs.so (declared in include/xs.h). Every step of the
+function of the same name in libxs.so (declared in include/xs/xs.h). Every step of the
 computation runs in the library's HIP kernels. There is no fallback path: if the library is
 not built, or the library rejects a call, these functions raise.
 
@@ -36,7 +36,7 @@ _i = ctypes.c_int
 _f = ctypes.c_float
 
 class XsStepDesc(ctypes.Structure):
-    """Mirror of xs_step_desc in include/xs.h (field order and types must match)."""
+    """Mirror of xs_step_desc in include/xs/xs.h (field order and types must match)."""
 
     _fields_ = [
         ("q", ctypes.c_void_p), ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),

@@ -8,7 +8,7 @@
 #include <string>
 #include <vector>
 
-#include "xs.h"
+#include "xs/xs.h"
 #include "xs_internal.h"
 
 #define XS_API extern "C" __attribute__((visibility("default")))

@@ -1,4 +1,4 @@
-"""C ABI checks that need no GPU: the library loads, exports what include/xs.h declares, and
+"""C ABI checks that need no GPU: the library loads, exports what include/xs/xs.h declares, and
 rejects bad arguments on the host with a status and a message, before any HIP call."""
 
 import ctypes
@@ -10,7 +10,7 @@ import pytest
 from paged_kv_decode_xs_amd import _binding as xb
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "xs.h")
+HEADER = os.path.join(ROOT, "include", "xs", "xs.h")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(xb.LIB_PATH), reason="libxs.so not built")
 

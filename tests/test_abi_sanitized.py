@@ -20,7 +20,7 @@ def _fresh() -> bool:
     if not os.path.exists(lib):
         return False
     t = os.path.getmtime(lib)
-    srcs = xb_build.sources() + [os.path.join(xb_build.INCLUDE, "xs.h")]
+    srcs = xb_build.sources() + [os.path.join(xb_build.INCLUDE, "xs", "xs.h")]
     srcs += [os.path.join(xb_build.CSRC, f) for f in os.listdir(xb_build.CSRC) if f.endswith(".h")]
     return all(os.path.getmtime(s) <= t for s in srcs)
 
