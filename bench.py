@@ -7,6 +7,9 @@ Qwen3-8B batch; every other decode workload gets a row of its own.
   value         K+V bytes the step must stream / measured step time, in GB/s (whole job, 1 GPU)
   ms_per_step   mean time of one step on the GPU (HIP events around K back-to-back steps)
   seqs_per_s    batch / step time
+  total_GBps    every algorithmic byte of the step (K+V, block ids, q, lengths, the append, the
+                split-K partials written and read, out) / step time
+  step_us_spread  p10 / p50 / p90 of the step time over groups of 10 back-to-back steps
   roofline      the decode kernel alone: its algorithmic bytes per launch / its mean duration,
                 which is one HIP event pair around K back-to-back decode launches (the fused
                 append + decode call, no reduce) on the launch stream; vs 8 TB/s.
@@ -280,6 +283,9 @@ def run_headline(w, P: int, fused: bool, K: int, warmup: int, copies=None) -> di
             s.attend(stream)
 
     ms_step = time_calls(step, K, stream)
+    # Spread of the step time: means of groups of 10 back-to-back steps (an event pair per group).
+    per_s = 10 if K >= 20 else max(1, K)
+    step_group_ms = [time_calls(lambda i, g=g: step(g * per_s + i), per_s, stream) for g in range(max(1, K // per_s))]
     ms_decode = time_calls(decode_only, K, stream)
     groups = 5 if K >= 10 else 1
     per = max(1, K // groups)
@@ -292,7 +298,8 @@ def run_headline(w, P: int, fused: bool, K: int, warmup: int, copies=None) -> di
     del steps
     torch.cuda.empty_cache()
     return {"case": case, "R": R, "ms_step": ms_step, "ms_decode": ms_decode, "ms_warm": ms_warm, "out": out,
-            "decode_group_us": [round(g * 1e3, 2) for g in group_ms]}
+            "decode_group_us": [round(g * 1e3, 2) for g in group_ms],
+            "step_group_us": [g * 1e3 for g in step_group_ms], "step_group_size": per_s}
 
 
 def decode_row(name: str, P: int, K: int, warmup: int, fused: bool = True, headline=None,
@@ -772,6 +779,13 @@ def main() -> int:
         },
         "seqs_per_s": round(w.batch / (ms_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100 * kv_gbs / HBM_PEAK_GBS, 2),
+        "total_GBps": round(ab["step"] / (ms_step * 1e-3) / 1e9, 2),
+        "step_us_spread": {
+            "p10": round(float(np.percentile(r["step_group_us"], 10)), 2),
+            "p50": round(float(np.percentile(r["step_group_us"], 50)), 2),
+            "p90": round(float(np.percentile(r["step_group_us"], 90)), 2),
+            "over": f"{len(r['step_group_us'])} groups of {r['step_group_size']} back-to-back steps, one event pair each",
+        },
         "warm_cache_kv_GBps": round(ab["kv"] / (r["ms_warm"] * 1e-3) / 1e9, 2),
         "achievable_read_GBps": achievable,
         "pct_of_achievable_nontemporal_read": round(100 * kv_gbs / achievable["nontemporal"], 2),
