@@ -44,7 +44,10 @@
  *     * block_size, and the block ids in use lie in [0, num_blocks). Violating them gives
  *     undefined results but no out-of-bounds access. The kernels clamp L_b to
  *     max_blocks_per_seq * block_size, skip blocks whose id lies outside [0, num_blocks),
- *     and treat L_b <= 0 as an empty context.
+ *     and treat L_b <= 0 as an empty context. The slot an append writes (position L_b - 1 of
+ *     sequence b) must lie neither inside another sequence's context nor be another sequence's
+ *     slot, or the results of both are undefined (a read races the write). The Python package's
+ *     check_device_inputs checks these conditions on a host copy of the tables.
  */
 #ifndef XS_H
 #define XS_H

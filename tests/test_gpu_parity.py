@@ -41,7 +41,8 @@ def test_workload_full_size(name):
     ref = OracleResult(case, w.partition_size)
     err0, _, _ = check_case(case, 0, ref, label=f"{name} unsplit")
     err1, _, _ = check_case(case, w.partition_size, ref, check_pools=False, label=f"{name} split")
-    err2, _, _ = check_case(case, w.partition_size, ref, label=f"{name} split fused", fused=True)
+    err2, step, _ = check_case(case, w.partition_size, ref, label=f"{name} split fused", fused=True)
+    assert step.check_inputs() == [], "the workload's tables break a device-resident precondition"
     log(f"[gpu] {name}: max |err| unsplit {err0:.3g}, split {err1:.3g}, split+fused append {err2:.3g}")
 
 
@@ -215,6 +216,8 @@ def test_bad_block_ids_are_skipped(P, fused):
     dev = case_to_device(case)
     dev["block_tables"].copy_(torch.from_numpy(bad))
     step = run_step(dev, w.scale, P, 64 if P else None, fused=fused)
+    problems = step.check_inputs()
+    assert len(problems) == 2 and "block_tables[0, 1] = -1" in problems[0] and f"= {NB + 5} " in problems[1], problems
     got = as_f64(step.out)
     assert np.isfinite(got).all()
     assert_close(got, exp, *TOL["bf16"], f"bad block ids P={P} fused={fused}")
@@ -233,6 +236,8 @@ def test_partition_overflow_gives_nan_rows():
     step = xs.DecodeStep(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["context_lens"],
                          dev["k_new"], dev["v_new"], w.scale, partition_size=64, max_context_len=128, fused=True)
     assert step.part_m.shape[-1] == 2
+    problems = step.check_inputs()
+    assert len(problems) == 1 and problems[0].startswith("sequence 1: 250 tokens need 4 partitions"), problems
     nan_fill(step)
     step.run()
     torch.cuda.synchronize()
