@@ -316,7 +316,9 @@ int xs_kv_swap_in(const void* k_host, const void* v_host, void* k_cache, void* v
  * so are positions whose block id is outside [0, num_blocks).
  * Arguments: k_src, v_src [batch, num_kv_heads, chunk_size, head_dim] (read); k_cache, v_cache
  * (written in place); block_tables [batch, max_blocks_per_seq], start_pos [batch], chunk_lens
- * [batch] (int32, device, read). XS_BF16 or XS_F32. Two positions must not map the same slot.
+ * [batch] (int32, device, read). XS_BF16 or XS_F32. Two positions must not map the same slot,
+ * and no appended slot may lie inside another sequence's context (a read would race the write);
+ * the Python package's check_prefill_inputs checks these conditions on a host copy of the tables.
  * batch == 0 or chunk_size == 0 is a no-op.
  */
 int xs_kv_append_chunk(const void* k_src, const void* v_src, void* k_cache, void* v_cache,

@@ -31,4 +31,5 @@ from ._binding import (  # noqa: F401
     xs_stream_read_probe,
     xs_version,
 )
-from .step import DecodeStep, StepGraph, check_device_inputs, suggest_partition_size  # noqa: F401
+from .checks import check_device_inputs, check_prefill_inputs  # noqa: F401
+from .step import DecodeStep, StepGraph, suggest_partition_size  # noqa: F401

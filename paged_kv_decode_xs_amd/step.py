@@ -9,9 +9,8 @@ xs_paged_attn_reduce_sinks.
 `DecodeStep.capture()` records the same step as one HIP graph (xs_step_graph_create); replaying it
 runs the step on the buffers as they are at replay time.
 `suggest_partition_size` picks a split partition size from a batch's context lengths (host side).
-`check_device_inputs` checks, on the host, the preconditions that live in device memory (lengths,
-block ids, the append's target blocks, the partition count); `DecodeStep.check_inputs` applies it
-to a step.
+`DecodeStep.check_inputs` checks, on the host, the step's preconditions that live in device memory
+(`checks.check_device_inputs`).
 """
 
 from __future__ import annotations
@@ -21,6 +20,7 @@ from typing import List, Optional, Sequence
 import torch
 
 from . import _binding as xb
+from .checks import check_device_inputs
 
 # Split items per compute unit that the partition-size rule aims at (at most).
 ITEMS_PER_CU = 12.5
@@ -47,60 +47,6 @@ def suggest_partition_size(context_lens: Sequence[int], num_kv_heads: int, block
     while P < longest and num_kv_heads * sum(-(-x // P) for x in lens) > ITEMS_PER_CU * num_cus:
         P *= 2
     return P
-
-
-def check_device_inputs(block_tables: torch.Tensor, context_lens: torch.Tensor, num_blocks: int, block_size: int,
-                        partition_size: int = 0, max_partitions: int = 0, limit: int = 20) -> List[str]:
-    """The step's preconditions that live in device memory, checked on the host.
-
-    The library cannot check these before a launch without a synchronisation, so a violation gives
-    undefined results instead of an error. This helper copies the tables to the host (it
-    synchronises) and returns one message per violation found, at most `limit`; an empty list
-    means none. It checks:
-    - 0 <= L_b <= max_blocks_per_seq * block_size;
-    - the ids of the blocks holding positions 0 .. L_b - 1 lie in [0, num_blocks);
-    - the slot that receives position L_b - 1 (the append's target) is neither inside another
-      sequence's context (that sequence would read it while it is written) nor another
-      sequence's target;
-    - with split-K (partition_size > 0), ceil(L_b / partition_size) <= max_partitions. A longer
-      sequence gets NaN rows."""
-    bt = block_tables.detach().to("cpu").numpy()
-    lens = context_lens.detach().to("cpu").numpy()
-    if bt.ndim != 2 or lens.ndim != 1 or bt.shape[0] != lens.shape[0]:
-        raise ValueError("block_tables must be [batch, max_blocks_per_seq] and context_lens [batch]")
-    mbps = bt.shape[1]
-    problems: List[str] = []
-
-    def note(msg: str) -> None:
-        if len(problems) < limit:
-            problems.append(msg)
-
-    users = {}  # block -> [(sequence, logical index)] over every block a context covers
-    targets = {}  # sequence -> (block, slot) of its position L_b - 1
-    for b, L in enumerate(int(x) for x in lens):
-        if L < 0 or L > mbps * block_size:
-            note(f"context_lens[{b}] = {L} is outside [0, {mbps * block_size}]")
-            continue
-        for j in range(-(-L // block_size)):
-            blk = int(bt[b, j])
-            if blk < 0 or blk >= num_blocks:
-                note(f"block_tables[{b}, {j}] = {blk} is outside [0, {num_blocks})")
-                continue
-            users.setdefault(blk, []).append((b, j))
-        if L >= 1:
-            targets[b] = (int(bt[b, (L - 1) // block_size]), (L - 1) % block_size)
-        if partition_size > 0 and -(-L // partition_size) > max_partitions:
-            note(f"sequence {b}: {L} tokens need {-(-L // partition_size)} partitions of {partition_size}, "
-                 f"max_partitions is {max_partitions}")
-    seen = {}
-    for b, (blk, slot) in targets.items():
-        if (blk, slot) in seen:
-            note(f"sequences {seen[(blk, slot)]} and {b} both append into block {blk}, slot {slot}")
-        seen.setdefault((blk, slot), b)
-        for c, j in users.get(blk, []):
-            if c != b and j * block_size + slot < int(lens[c]):
-                note(f"block {blk}, slot {slot} receives sequence {b}'s new token inside sequence {c}'s context")
-    return problems
 
 
 class DecodeStep:

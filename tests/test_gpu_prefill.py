@@ -92,6 +92,7 @@ def _full_check(w, label, split=None):
     exp = oracle.paged_prefill_attention(case.q, kp, vp, case.block_tables, case.start_pos, case.chunk_lens, w.scale,
                                          w.block_size, "bf16")
     dev = _to_dev(case)
+    assert xs.check_prefill_inputs(dev["bt"], dev["sp"], dev["cl"], w.chunk, case.k_cache.shape[0], w.block_size) == []
     out = _run(dev, w.scale, split)
     _check_pools(dev, kp, vp)
     got = as_f64(out)
@@ -175,6 +176,8 @@ def test_prefill_dispatch_orders(order, split):
     for b in bad:
         dev["sp"][b] = -5
         exp[b] = 0.0
+    problems = xs.check_prefill_inputs(dev["bt"], dev["sp"], dev["cl"], C, case.k_cache.shape[0], BS)
+    assert [p.split(":")[0] for p in problems] == [f"sequence {b}" for b in bad], problems
     out = _run(dev, w.scale, split)
     got = as_f64(out)
     assert_close(got, exp, *TOL["bf16"], f"prefill order {order} split={split}")
