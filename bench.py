@@ -692,7 +692,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build runs every step on a single device and has no "
+        print("bench.py measures one GPU: the library runs every step on a single device and has no "
               "multi-GPU path (run with --gpus 1)", file=sys.stderr)
         return 2
 

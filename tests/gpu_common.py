@@ -64,7 +64,7 @@ class OracleResult:
 
 def check_rounding_bound(got: np.ndarray, ref: "OracleResult", what: str) -> None:
     """bf16 outputs: the per-element bound of the kernels' rounding (tests/rounding_bound.py), which
-    at long contexts is far tighter than the spec bar."""
+    at long contexts is far tighter than the output tolerance."""
     case = ref._case
     w = case.workload
     if w.dtype != "bf16":

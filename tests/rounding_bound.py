@@ -1,6 +1,6 @@
 """A per-element error bound for the bf16 attention outputs, derived from the kernels' own rounding.
 
-The spec bar (2e-2 absolute + 2e-2 relative) cannot tell a right long-context result from a
+The output tolerance (2e-2 absolute + 2e-2 relative) cannot tell a right long-context result from a
 wrong one: with N(0, 1) data the output of a row over L keys has a spread of about sqrt(e / L),
 0.009 at L = 32768, so a kernel that skipped a whole block (or a 512-token partition) would still
 pass it. The bound below is what the arithmetic of the matrix-core kernels allows, and no more.
@@ -23,7 +23,7 @@ round the weights (the fp32 and generic bf16 decode) satisfy it a fortiori.
 
 tau is about sqrt(e / L) u-sized for N(0, 1) data, i.e. it shrinks with the context like the
 output itself, which is what gives the bound its power (tests/test_rounding_bound.py shows a
-dropped block failing it at the long-context sizes where the spec bar passes).
+dropped block failing it at the long-context sizes where the output tolerance passes).
 
 The spread tau is computed here from the oracle's gather (decode_values, gather_kv) and the plain
 softmax; it is test machinery, not the oracle's arithmetic.

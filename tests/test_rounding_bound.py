@@ -1,7 +1,7 @@
 """The rounding bound of tests/rounding_bound.py: its spread in closed form, a simulation of the
 kernels' rounding that satisfies it, and its power: at the long-context sizes (the 64-sequence
 batch's longest rows, the 32K row of the long-context batch) an output that misses one 16-token
-block, or one 512-token partition, violates it, while the spec bar alone lets them pass.
+block, or one 512-token partition, violates it, while the output tolerance alone lets them pass.
 CPU only."""
 
 import numpy as np
@@ -92,7 +92,7 @@ def test_kernel_like_rounding_passes_and_dropped_keys_fail(L, P):
         n = rb.violations(wrong, ref, tau)
         assert n > 0, f"L={L}: dropping {drop} keys goes unnoticed by the rounding bound"
         if drop * 64 <= L:
-            # A sixty-fourth of the keys or less: the spec bar alone cannot see it.
+            # A sixty-fourth of the keys or less: the output tolerance alone cannot see it.
             assert np.all(np.abs(wrong - ref) <= atol + rtol * np.abs(ref))
 
 
