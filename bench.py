@@ -259,6 +259,35 @@ def time_calls(fn, K: int, stream) -> float:
     return a.elapsed_time(b) / K
 
 
+def read_probe() -> dict:
+    """Reference read rate of the device: the library's streaming-read probe over 2 GiB, plain and
+    nontemporal, in both of its shapes (best of 5 single calls each); the faster shape is the rate.
+    It runs first, on a fresh allocation: the narrow shape, fastest in a sweep, reads slower on a
+    buffer carved from memory that the pools have already cycled through."""
+    import torch
+
+    import paged_kv_decode_xs_amd as xs
+
+    stream = torch.cuda.current_stream()
+    probe_buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    probe_buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    achievable = {}
+    for nt in (False, True):
+        for shape in (0, 1):
+            call = lambda i, nt=nt, shape=shape: xs.xs_stream_read_probe(probe_buf, sink, nontemporal=nt, shape=shape,
+                                                                         stream=stream)
+            call(0)
+            best = min(time_calls(call, 1, stream) for _ in range(5))
+            achievable[("nontemporal" if nt else "plain") + ("_narrow" if shape else "_wide")] = round(
+                probe_buf.numel() / (best * 1e-3) / 1e9, 1)
+        key = "nontemporal" if nt else "plain"
+        achievable[key] = max(achievable[key + "_wide"], achievable[key + "_narrow"])
+    del probe_buf, sink
+    torch.cuda.synchronize()
+    return achievable
+
+
 def run_headline(w, P: int, fused: bool, K: int, warmup: int, copies=None) -> dict:
     """The headline workload: K back-to-back steps (append + decode + reduce) on rotated pools;
     then K back-to-back decode launches alone (the roofline's duration), in groups whose means
@@ -725,21 +754,11 @@ def main() -> int:
     w = wl.WORKLOADS[args.workload]
     P = dict(CONFIGS).get(w.name, w.partition_size) if args.partition is None else args.partition
     K = args.steps
+    achievable = read_probe()
     r = run_headline(w, P, fused, K, args.warmup, args.copies)
     case, R, ms_step, ms_decode = r["case"], r["R"], r["ms_step"], r["ms_decode"]
     stream = torch.cuda.current_stream()
 
-    # Reference read rate of the device: the library's streaming-read probe over 2 GiB.
-    probe_buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
-    probe_buf.fill_(1)
-    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
-    achievable = {}
-    for nt in (False, True):
-        xs.xs_stream_read_probe(probe_buf, sink, nontemporal=nt, stream=stream)
-        best = min(time_calls(lambda i: xs.xs_stream_read_probe(probe_buf, sink, nontemporal=nt, stream=stream), 1,
-                              stream) for _ in range(5))
-        achievable["nontemporal" if nt else "plain"] = round(probe_buf.numel() / (best * 1e-3) / 1e9, 1)
-    del probe_buf
 
     if args.copy_calibration:
         _copy_calibration()

@@ -409,12 +409,14 @@ int xs_paged_attn_prefill_sinks(const void* q, const void* k_cache, const void* 
 
 /*
  * Measurement aid, not part of the decode step: reads `bytes` (a multiple of 16) at `buf` with
- * 16-byte loads (nontemporal if `nontemporal` != 0), each workgroup taking whole 64 KiB chunks,
- * and writes at most one word to `sink` (device memory, 4 bytes). Timing it gives the read rate
- * that contiguous streaming reaches on the device, the reference the decode kernel's bandwidth
- * is compared with. `buf` must be 16-byte aligned.
+ * 16-byte loads (nontemporal if `nontemporal` != 0) and writes at most one word to `sink` (device
+ * memory, 4 bytes). Workgroups take chunks of the buffer in turn: shape 0 runs 16 workgroups per
+ * CU on 256 KiB chunks, shape 1 two workgroups per CU on 16 KiB chunks (any other shape is
+ * XS_EINVAL). Timing both and taking the faster gives the read rate that contiguous streaming
+ * reaches on the device, the reference the decode kernel's bandwidth is compared with. `buf` must
+ * be 16-byte aligned.
  */
-int xs_stream_read_probe(const void* buf, size_t bytes, unsigned* sink, int nontemporal, void* stream);
+int xs_stream_read_probe(const void* buf, size_t bytes, unsigned* sink, int nontemporal, int shape, void* stream);
 
 /* Message for the last nonzero status returned on this thread ("" if none). Host memory owned
  * by the library, valid until the next call on this thread. */

@@ -63,7 +63,7 @@ SIGNATURES = {
     "xs_paged_attn_decode_sinks": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _f, _vp, _vp, _vp, _vp,
                                    _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp],
     "xs_paged_attn_reduce_sinks": [_vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _vp],
-    "xs_stream_read_probe": [_vp, ctypes.c_size_t, _vp, _i, _vp],
+    "xs_stream_read_probe": [_vp, ctypes.c_size_t, _vp, _i, _i, _vp],
     "xs_kv_swap_out": [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp],
     "xs_kv_swap_in": [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp],
     "xs_step_graph_create": [ctypes.POINTER(XsStepDesc), _i, ctypes.POINTER(ctypes.c_void_p)],
@@ -309,13 +309,15 @@ def xs_paged_attn_reduce_sinks(part_o: torch.Tensor, part_m: torch.Tensor, part_
         B, Hq, D, int(partition_size), NP, _dtype_code(out), _stream_handle(stream)))
 
 
-def xs_stream_read_probe(buf: torch.Tensor, sink: torch.Tensor, nontemporal: bool = True, stream=None) -> None:
-    """Read all of `buf` with 16-byte loads (a bandwidth reference); `sink` is a 4-byte device buffer."""
+def xs_stream_read_probe(buf: torch.Tensor, sink: torch.Tensor, nontemporal: bool = True, shape: int = 0,
+                         stream=None) -> None:
+    """Read all of `buf` with 16-byte loads (a bandwidth reference); `sink` is a 4-byte device buffer.
+    shape 0: 16 workgroups per CU on 256 KiB chunks; shape 1: two per CU on 16 KiB chunks."""
     _dev(buf, sink)
     nbytes = buf.numel() * buf.element_size()
     _need(sink.numel() * sink.element_size() >= 4, "sink must hold 4 bytes")
     _check("xs_stream_read_probe", load_library().xs_stream_read_probe(
-        _ptr(buf), nbytes - nbytes % 16, _ptr(sink), int(bool(nontemporal)), _stream_handle(stream)))
+        _ptr(buf), nbytes - nbytes % 16, _ptr(sink), int(bool(nontemporal)), int(shape), _stream_handle(stream)))
 
 
 def _swap_checks(k_cache, v_cache, k_host, v_host, src, dst):

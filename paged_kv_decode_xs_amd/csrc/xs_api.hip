@@ -355,13 +355,16 @@ XS_API int xs_paged_attn_reduce(const float* part_o, const float* part_m, const 
                                                     static_cast<hipStream_t>(stream)));
 }
 
-XS_API int xs_stream_read_probe(const void* buf, size_t bytes, unsigned* sink, int nontemporal, void* stream) {
+XS_API int xs_stream_read_probe(const void* buf, size_t bytes, unsigned* sink, int nontemporal, int shape,
+                                void* stream) {
   const char* who = "xs_stream_read_probe";
   if (!buf || !sink) return fail(XS_EINVAL, "%s: buf and sink must not be NULL", who);
   if (!aligned16(buf) || bytes % 16 != 0) return fail(XS_EINVAL, "%s: buf must be 16-byte aligned and bytes a multiple of 16", who);
+  if (shape != 0 && shape != 1) return fail(XS_EINVAL, "%s: shape = %d (0 or 1)", who, shape);
   if (bytes == 0) return ok();
   (void)hipGetLastError();
-  return launch_status(who, xs::launch_stream_read(buf, bytes, sink, nontemporal != 0, static_cast<hipStream_t>(stream)));
+  return launch_status(who, xs::launch_stream_read(buf, bytes, sink, nontemporal != 0, shape,
+                                                   static_cast<hipStream_t>(stream)));
 }
 
 // ------------------------------------------------------------------------------------------

@@ -122,7 +122,8 @@ int prefill_row_blocks(int chunk, int group);
 hipError_t launch_paged_prefill(const PrefillArgs& a, hipStream_t stream);
 
 // Streaming-read probe over `bytes` (a multiple of 16) of device memory.
-hipError_t launch_stream_read(const void* buf, size_t bytes, unsigned* sink, bool nontemporal, hipStream_t stream);
+hipError_t launch_stream_read(const void* buf, size_t bytes, unsigned* sink, bool nontemporal, int shape,
+                              hipStream_t stream);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();

@@ -137,10 +137,13 @@ def test_binding_raises_without_library(tmp_path):
 
 def test_probe_rejects():
     lib = xb.load_library()
-    assert lib.xs_stream_read_probe(None, 64, FAKE, 1, None) == 1
+    assert lib.xs_stream_read_probe(None, 64, FAKE, 1, 0, None) == 1
     assert "NULL" in xb.xs_last_error()
-    assert lib.xs_stream_read_probe(FAKE, 24, FAKE, 1, None) == 1
+    assert lib.xs_stream_read_probe(FAKE, 24, FAKE, 1, 0, None) == 1
     assert "multiple of 16" in xb.xs_last_error()
+    assert lib.xs_stream_read_probe(FAKE, 64, FAKE, 1, 2, None) == 1
+    assert "shape = 2" in xb.xs_last_error()
+    assert lib.xs_stream_read_probe(FAKE, 0, FAKE, 1, 1, None) == 0  # nothing to read: no launch
 
 
 def test_decode_append_rejects_missing_new_rows():
