@@ -61,7 +61,7 @@ DECODE_SOURCES = ["paged_kv_decode_xs_amd/csrc/xs_decode.hip", "paged_kv_decode_
 HEADLINE = "qwen3_8b_b64"
 # The specification's five decode workloads, in its order, with the partition size each step uses
 # (0: unsplit, one launch; the fp32 GPT-2 step is 32 tokens).
-CONFIGS = [("gpt2_fp32_ctx32", 0), ("gpt2_bf16_b8", 128), ("qwen3_8b_b1_ctx4096", 128), ("qwen3_8b_b64", 1024),
+CONFIGS = [("gpt2_fp32_ctx32", 0), ("gpt2_bf16_b8", 128), ("qwen3_8b_b1_ctx4096", 64), ("qwen3_8b_b64", 1024),
            ("qwen3_8b_b4_long", 512)]
 # Further decode workloads measured like the config rows.
 EXTRA_WORKLOADS = [("qwen3_8b_b64_tp8_share", 256), ("gptoss_20b_window128_b64", 0)]

@@ -147,6 +147,9 @@ def test_suggested_partition_sizes_match_the_measured_best():
     tp = wl.WORKLOADS["qwen3_8b_b64_tp8_share"]
     lens = wl.make_layout(tp, np.random.default_rng(tp.seed)).context_lens
     assert suggest_partition_size(lens, tp.num_kv_heads, tp.block_size) == 128
+    # One 4096-token Qwen3-8B sequence: 64 measured fastest (11.32 us per step against 11.81 at 128).
+    one = wl.WORKLOADS["qwen3_8b_b1_ctx4096"]
+    assert suggest_partition_size([4096], one.num_kv_heads, one.block_size) == 64 == one.partition_size
 
 
 def test_suggested_partition_size_edges():

@@ -115,7 +115,7 @@ WORKLOADS: Dict[str, Workload] = {
             "head_dim 128, context 4096, block_size 16, scattered blocks, RMS-normalised q/k",
             dtype="bf16", batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
             ctx=("fixed", [4096]), num_blocks=None, max_blocks_per_seq=256, values="rmsnorm_gain",
-            seed=2, partition_size=128,
+            seed=2, partition_size=64,
         ),
         Workload(
             name="qwen3_8b_b64",
