@@ -31,8 +31,6 @@ softmax; it is test machinery, not the oracle's arithmetic.
 
 from __future__ import annotations
 
-from typing import Optional
-
 import numpy as np
 
 import oracle

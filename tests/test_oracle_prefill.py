@@ -17,7 +17,7 @@ import oracle.paged_attention as plain
 import oracle.prefill as prefill_mod
 import oracle.sinks_window as sinks_mod
 from oracle.brute_force import brute_decode_attention, brute_decode_attention_sinks
-from tests.oracle_pins import _bf16_bits, _flat_scatter, _rand_case, _values_torch
+from tests.oracle_pins import _bf16_bits, _rand_case, _values_torch
 from tests.oracle_pins_sinks import _sink_vals, _sinks
 
 
