@@ -618,15 +618,21 @@ __global__ __launch_bounds__(64 * kWaves) void paged_prefill_kernel(PrefillParam
 }
 
 // Split-K merge of the rows of split row blocks (the others were written by the attention
-// kernel): 32 lanes per row, four consecutive d each. Row (b, h, i) combines the pieces that hold
-// keys it sees (pieces 0 .. pos / (64 PT)): M = max_j m_j, w_j = l_j 2^(m_j - M),
+// kernel): D/E lanes per row, E consecutive d each (E = 4 or 8). Row (b, h, i) combines the pieces
+// that hold keys it sees (pieces 0 .. pos / (64 PT)): M = max_j m_j, w_j = l_j 2^(m_j - M),
 // out = sum_j w_j o_j / sum_j w_j, taken four pieces at a time (their loads in flight together)
 // with a running maximum. SW: the pieces start at the one holding the row's first window key,
 // and the sink enters as one more term of weight 2^(sigma - M) with no value row.
+// The merge is a chain of dependent loads (the lengths, then the partials). E = 8 halves the
+// wavefronts at the cost of a longer chain per lane: it pays where the E = 4 grid would take
+// several rounds of resident workgroups (measured: 14.6 -> 10.6 us on the Qwen3 batch's rows),
+// not where one round holds it (the 16K chunk: 204 -> 209 us per call).
 constexpr int kMergeThreads = 256;
-template <int D, bool SW>
+template <int D, bool SW, int E>
 __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillParams prm) {
-  constexpr int LPR = D / 4;                  // lanes per row
+  static_assert(E == 4 || E == 8, "four or eight d per lane");
+  constexpr int NV = E / 4;                 // float4 pieces of a partial row per lane
+  constexpr int LPR = D / E;                // lanes per row
   constexpr int RPB = kMergeThreads / LPR;  // rows per workgroup
   const int sub = threadIdx.x % LPR;
   const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;  // (b * Hq + h) * C + i
@@ -656,16 +662,20 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillPar
       wsum = 1.f;
     }
   }
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
   for (int j0 = jfirst; j0 < nrow; j0 += 4) {
     float2 ml[4];
-    float4 o[4];
+    float4 o[4][NV];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const bool in = j0 + u < nrow;
       const size_t pr = prow0 + (in ? j0 + u : 0);
       ml[u] = prm.part_ml[pr];
-      o[u] = reinterpret_cast<const float4*>(prm.part_o + pr * D)[sub];
+      const float4* src = reinterpret_cast<const float4*>(prm.part_o + pr * D) + NV * sub;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) o[u][v] = src[v];
       if (!in) ml[u] = make_float2(-INFINITY, 0.f);
     }
     float Mn = M;
@@ -674,18 +684,28 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillPar
     if (Mn == -INFINITY) continue;  // no keys yet
     const float f = fast_exp2(M - Mn);  // 0 while M is still -inf
     wsum *= f;
-    acc = make_float4(acc.x * f, acc.y * f, acc.z * f, acc.w * f);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] *= f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const float w = ml[u].y * fast_exp2(ml[u].x - Mn);  // 0 for a piece with none of the row's keys
       wsum += w;
-      acc = make_float4(fmaf(w, o[u].x, acc.x), fmaf(w, o[u].y, acc.y), fmaf(w, o[u].z, acc.z), fmaf(w, o[u].w, acc.w));
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        acc[4 * v] = fmaf(w, o[u][v].x, acc[4 * v]);
+        acc[4 * v + 1] = fmaf(w, o[u][v].y, acc[4 * v + 1]);
+        acc[4 * v + 2] = fmaf(w, o[u][v].z, acc[4 * v + 2]);
+        acc[4 * v + 3] = fmaf(w, o[u][v].w, acc[4 * v + 3]);
+      }
     }
     M = Mn;
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  reinterpret_cast<uint2*>(prm.out)[(size_t)row * (D / 4) + sub] =
-      make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
+  uint2* dst = reinterpret_cast<uint2*>(prm.out) + (size_t)row * (D / 4) + NV * sub;
+#pragma unroll
+  for (int v = 0; v < NV; ++v)
+    dst[v] = make_uint2(pack_bf16x2(acc[4 * v] * inv, acc[4 * v + 1] * inv),
+                        pack_bf16x2(acc[4 * v + 2] * inv, acc[4 * v + 3] * inv));
 }
 
 template <int D, bool SW>
@@ -695,9 +715,15 @@ hipError_t launch_prefill_d(const PrefillParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((paged_prefill_kernel<D, SW>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, p);
   if (p.part_tiles > 0) {
     const long long rows = (long long)p.batch * p.num_q_heads * p.chunk;
-    constexpr int rpb = kMergeThreads / (D / 4);
-    hipLaunchKernelGGL((prefill_merge_kernel<D, SW>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(kMergeThreads),
-                       0, stream, p);
+    // Eight d per lane when four would need more workgroups than one resident round (eight
+    // 256-thread workgroups per CU).
+    constexpr int rpb4 = kMergeThreads / (D / 4), rpb8 = kMergeThreads / (D / 8);
+    if ((rows + rpb4 - 1) / rpb4 > 8LL * device_cu_count())
+      hipLaunchKernelGGL((prefill_merge_kernel<D, SW, 8>), dim3((unsigned)((rows + rpb8 - 1) / rpb8)),
+                         dim3(kMergeThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((prefill_merge_kernel<D, SW, 4>), dim3((unsigned)((rows + rpb4 - 1) / rpb4)),
+                         dim3(kMergeThreads), 0, stream, p);
   }
   return hipGetLastError();
 }

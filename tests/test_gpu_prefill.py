@@ -251,7 +251,8 @@ def test_append_chunk_f32_bit_exact():
 
 
 @pytest.mark.parametrize("name,split", [("qwen3_8b_prefill_c512", None), ("qwen3_8b_prefill_c512", 512),
-                                        ("qwen3_8b_prefill_c512", 1024), ("qwen3_8b_prefill_long16k", None),
+                                        ("qwen3_8b_prefill_c512", 1024), ("qwen3_8b_prefill_c512", 2048),
+                                        ("qwen3_8b_prefill_long16k", None), ("qwen3_8b_prefill_long16k", 4096),
                                         ("qwen3_8b_prefill_long16k", 2048), ("qwen3_8b_prefill_long16k", 1024)])
 def test_qwen3_prefill_workload_sampled_rows(name, split):
     w = PREFILL_WORKLOADS[name]

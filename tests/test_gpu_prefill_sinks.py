@@ -142,7 +142,7 @@ def test_prefill_sinks_reduces_to_plain_bits(shape):
 
 
 # Full-size gpt-oss layer shapes: sampled rows of the chunk (every head) against the oracle.
-SAMPLED = {"gptoss_20b_prefill_window128_c512": (0, 64, 128), "gptoss_20b_prefill_full_c512": (0, 256)}
+SAMPLED = {"gptoss_20b_prefill_window128_c512": (0, 64, 128), "gptoss_20b_prefill_full_c512": (0, 256, 2048)}
 
 
 @pytest.mark.parametrize("name,split", [(n, s) for n, splits in SAMPLED.items() for s in splits])
