@@ -24,7 +24,7 @@ from tests.rounding_bound import assert_rounding_bound, prefill_spread
 from tests.test_gpu_prefill import SHAPES, _shape_workload, _to_dev
 from workloads import f32_to_bf16_bits
 from workloads.device import to_torch
-from workloads.prefill import PREFILL_WORKLOADS, make_prefill_case
+from workloads.prefill import PREFILL_WORKLOADS, PrefillWorkload, make_prefill_case
 
 pytestmark = pytest.mark.gpu
 
@@ -170,3 +170,60 @@ def test_prefill_sinks_gptoss_sampled_rows(name, split):
                                                        np.array([k], np.int32), w.scale, w.block_size, "bf16",
                                                        sinks=case.sinks, window=w.window)
             assert_close(got[b:b + 1, :, a:a + k], exp, atol, rtol, f"{name} b={b} rows {a}..{a + k} split={split}")
+
+
+# The merge of split rows runs eight d per lane when its four-wide grid would exceed one round of
+# resident workgroups (more than 8 * 256 * 8 rows at head_dim 128, 8 * 256 * 16 at 64). The shapes
+# above reach that width only with head_dim 64 and sinks; these two reach it with head_dim 128
+# and a window and sinks, and with head_dim 64 and neither. Sampled rows against the oracle.
+WIDE_MERGE = [
+    # Hq, Hkv, D, window, sinks: 2 x Hq x 512 rows
+    (32, 8, 128, 300, True),   # 32 768 rows: 4096 workgroups of 8 rows at four d per lane
+    (64, 8, 64, 0, False),     # 65 536 rows: 4096 workgroups of 16 rows
+]
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,window,sinks", WIDE_MERGE)
+def test_wide_merge_sampled_rows(Hq, Hkv, D, window, sinks):
+    w = PrefillWorkload(name="wide_merge", description="", dtype="bf16", num_q_heads=Hq, num_kv_heads=Hkv,
+                        head_dim=D, block_size=16, chunk=512, start_pos=(1800, 700), chunk_lens=(512, 509),
+                        max_blocks_per_seq=160, seed=61, window=window, sinks=sinks)
+    rows = w.batch * Hq * w.chunk
+    assert rows // (256 // (D // 4)) > 8 * 256, "the shape must take the eight-wide merge"
+    split = 512
+    log(f"[gpu] prefill wide merge Hq={Hq} D={D} window={window} sinks={sinks} split={split}")
+    case = make_prefill_case(w)
+    kp, vp = oracle.kv_append_chunk(case.k_cache, case.v_cache, case.k_src, case.v_src, case.block_tables,
+                                    case.start_pos, case.chunk_lens, w.block_size)
+    dev = _to_dev(case)
+    _append(dev)
+    if window or sinks:
+        out = _attend(dev, case, window, split)
+    else:
+        B, Hq_, C, D_ = dev["q"].shape
+        NP = xs.num_partitions(dev["bt"].shape[1] * w.block_size, split)
+        out = torch.full_like(dev["q"], float("nan"))
+        po = torch.full((B, Hq_, C, NP, D_), float("nan"), dtype=torch.float32, device="cuda")
+        pml = torch.full((B, Hq_, C, NP, 2), float("nan"), dtype=torch.float32, device="cuda")
+        xs.xs_paged_attn_prefill_split(dev["q"], dev["k_cache"], dev["v_cache"], dev["bt"], dev["sp"], dev["cl"],
+                                       w.scale, split, out=out, part_o=po, part_ml=pml)
+    torch.cuda.synchronize()
+    got = as_f64(out)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(62)
+    atol, rtol = TOL["bf16"]
+    for b in range(w.batch):
+        n = int(case.chunk_lens[b])
+        assert not got[b, :, n:].any(), f"rows past chunk_lens[{b}] = {n} are not zero"
+        for a in sorted({0, n - 3, *rng.integers(1, n - 3, 2).tolist()}):
+            k = 3
+            sub_q = np.ascontiguousarray(case.q[b:b + 1, :, a:a + k])
+            start = np.array([int(case.start_pos[b]) + a], np.int32)
+            if window or sinks:
+                exp = oracle.paged_prefill_attention_sinks(sub_q, kp, vp, case.block_tables[b:b + 1], start,
+                                                           np.array([k], np.int32), w.scale, w.block_size, "bf16",
+                                                           sinks=case.sinks, window=window)
+            else:
+                exp = oracle.paged_prefill_attention(sub_q, kp, vp, case.block_tables[b:b + 1], start,
+                                                     np.array([k], np.int32), w.scale, w.block_size, "bf16")
+            assert_close(got[b:b + 1, :, a:a + k], exp, atol, rtol, f"wide merge D={D} b={b} rows {a}..{a + k - 1}")
