@@ -566,7 +566,7 @@ def swap_row(reps: int = 10) -> dict:
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-PREFILL_SPLITS = {"qwen3_8b_prefill_c512": (1024, 2048), "qwen3_8b_prefill_long16k": (1024, 2048, 4096),
+PREFILL_SPLITS = {"qwen3_8b_prefill_c512": (1024, 2048, 2560), "qwen3_8b_prefill_long16k": (1024, 2048, 4096),
                   "gptoss_20b_prefill_full_c512": (1024, 2048)}
 # Prefill rows of the result line: key -> workload.
 PREFILL_ROWS = {"chunked_prefill": "qwen3_8b_prefill_c512", "chunked_prefill_long": "qwen3_8b_prefill_long16k",
