@@ -103,6 +103,7 @@ def _mutate_sw(name):
     return mod
 
 
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")
 @pytest.mark.parametrize("name", sorted(SW_MUTANTS))
 def test_sinks_window_mutant_is_caught(name):
     mod = _mutate_sw(name)
