@@ -112,3 +112,29 @@ def test_unsplit_decode_needs_a_q_shaped_out(rec):
 def test_device_check_rejects_host_tensors():
     with pytest.raises(ValueError, match="on the GPU"):
         xb._dev(torch.zeros(4))
+
+
+@pytest.mark.parametrize("P,fused,sw,expected", [
+    (0, False, False, ["xs_kv_append", "xs_paged_attn_decode"]),
+    (0, True, False, ["xs_paged_attn_decode_append"]),
+    (64, False, False, ["xs_kv_append", "xs_paged_attn_decode", "xs_paged_attn_reduce"]),
+    (64, True, False, ["xs_paged_attn_decode_append", "xs_paged_attn_reduce"]),
+    (0, True, True, ["xs_paged_attn_decode_sinks"]),
+    (64, False, True, ["xs_kv_append", "xs_paged_attn_decode_sinks", "xs_paged_attn_reduce_sinks"]),
+    (64, True, True, ["xs_paged_attn_decode_sinks", "xs_paged_attn_reduce_sinks"]),
+])
+def test_decode_step_call_chain(rec, P, fused, sw, expected):
+    from paged_kv_decode_xs_amd.step import DecodeStep
+
+    a = _decode_inputs()
+    sinks = torch.zeros(8, dtype=torch.bfloat16) if sw else None
+    step = DecodeStep(a["q"], a["k"], a["v"], a["bt"], a["cl"], a["kn"], a["vn"], 0.125, partition_size=P,
+                      max_context_len=200 if P else None, fused=fused, sinks=sinks, window=16 if sw else 0)
+    step.run(stream=0)
+    assert [name for name, _ in rec.calls] == expected
+    if P:
+        assert step.part_m.shape == (3, 8, 4)  # ceil(200 / 64) partitions
+    if sw:
+        # The fused windowed decode gets k_new / v_new; the separate one gets none (the append ran).
+        sink_call = [args for name, args in rec.calls if name == "xs_paged_attn_decode_sinks"][0]
+        assert (sink_call[1] is not None) == fused
